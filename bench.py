@@ -1,0 +1,234 @@
+"""Throughput of the Compressed-PagedAttention compression step on one GPU.
+
+A step is one whole compression pass over the batch: zp_compress (score +
+select, then K/V compaction) followed by zp_update_global, for every
+(request, layer, KV head) unit of the workload. The default workload is the
+8B-like shape: 128 requests x 32 layers x 8 KV heads (32 query heads),
+head_dim 128, b = 16, N_max = 256 (4096 tokens, keep 4080), w = 32, bf16
+K/V/Q with near-duplicate keys, shuffled block tables. Inputs are resident in
+HBM before timing starts; the pools are compacted in place, so each step
+compresses the previous step's output (same shape, same trigger point).
+
+Prints one JSON line: tokens compressed per second (value), algorithmic HBM
+GB/s of the whole step, a roofline entry for the dominant kernel (kernel
+durations from HIP events recorded on the launch stream during the timed
+steps) and the CPU oracle timed on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+       [--cpu-seconds S] [--no-cpu]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "KV tokens compressed/sec + achieved HBM GB/s (frac of peak), 1 MI355X"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="8b_32L_8kv_32q_N4096")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    return ap.parse_args()
+
+
+def unit_bytes(spec, M: np.ndarray) -> dict:
+    """Algorithmic bytes per unit, summed over units, for one step.
+
+    whole step: s*d*(N + 4M) + s_q*w*G*d + 12*N_cap (keys read once, moved K
+    and V rows read and written, the window, global read for scoring plus the
+    read and write of the update); per kernel:
+      score_select: s*d*N + s_q*w*G*d + 4N (global) + 4N (attn out) + 4k (keep)
+      compact:      4*M*d*s + 4*M (keep entries of moved rows)
+      global:       8*N_cap + 8k (row read/write, keep and attn at kept)
+    """
+    s = 2 if spec.dtype == "bf16" else 4
+    d, N, k = spec.head_dim, spec.n_tokens, spec.keep
+    G = spec.q_heads // spec.kv_heads
+    wGd = spec.window * G * d * s
+    U = M.size
+    n_cap = N
+    Msum = float(M.sum())
+    return {
+        "step": U * (s * d * N + wGd + 12 * n_cap) + 4.0 * s * d * Msum,
+        "score_select": U * (s * d * N + wGd + 4 * N + 4 * N + 4 * k),
+        "compact": 4.0 * s * d * Msum + 4.0 * Msum,
+        "global_update": U * (8 * n_cap + 8 * k),
+    }
+
+
+def cpu_baseline(spec, wl, seconds: float) -> dict:
+    """The oracle, unchanged, on a bounded seeded sample of units."""
+    import oracle as O
+    import torch
+    from threadpoolctl import threadpool_limits
+    from kv_cache_compression_paged_amd import synth
+    R, L, H, b = spec.requests, spec.layers, spec.kv_heads, spec.block_size
+    n, k = spec.n_tokens, spec.keep
+    G = spec.q_heads // H
+    rng = np.random.default_rng(spec.seed + 99)
+    order = rng.permutation(R * L * H)
+    p = O.Params(n_max=spec.n_max, block_size=b, window=spec.window)
+    tab = torch.from_numpy(wl.tables).to(wl.k_pool.device)
+    done, t_cpu = 0, 0.0
+    with threadpool_limits(limits=1):
+        for u in order:
+            if t_cpu >= seconds and done >= 2:
+                break
+            u = int(u)
+            r, l, h = u // (L * H), (u // H) % L, u % H
+            blocks = tab[r].long()
+            kr = synth.raw_numpy(wl.k_pool[l, blocks, h].reshape(n, -1))
+            vr = synth.raw_numpy(wl.v_pool[l, blocks, h].reshape(n, -1))
+            q = synth.raw_numpy(wl.q_window[r, l, :, h * G:(h + 1) * G])
+            g = wl.global_scores[r, l, h].cpu().numpy()
+            pk = kr.reshape(1, spec.n_max, 1, b, -1)
+            pv = vr.reshape(1, spec.n_max, 1, b, -1)
+            t0 = time.perf_counter()
+            res = O.score_unit(O.widen(q, spec.dtype), O.widen(kr, spec.dtype),
+                               g.astype(np.float64), n, 0, p)
+            nk, nv = pk.copy(), pv.copy()
+            table = list(range(spec.n_max))
+            O.compact_unit(pk, nk, table, table, 0, 0, res.keep, b)
+            O.compact_unit(pv, nv, table, table, 0, 0, res.keep, b)
+            O.update_global(g, res.attn, res.keep, k)
+            t_cpu += time.perf_counter() - t0
+            done += 1
+    tokens_per_s = done * n / (L * H) / t_cpu
+    return {"value": tokens_per_s, "unit": "tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{done} seeded (request, layer, kv_head) units of this "
+                      f"workload, full oracle chain (score, select, K/V "
+                      f"compaction, global update), {t_cpu:.1f} s on one "
+                      f"thread; a token covers {L * H} units"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the "
+              "compression path needs no collective, see the design notes on "
+              "sharding.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import kv_cache_compression_paged_amd as Z
+    from kv_cache_compression_paged_amd import synth
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    Z.lib()
+    spec = synth.SPECS[args.workload]
+    dev = "cuda"
+    print(f"[bench] generating {spec.name}", file=sys.stderr, flush=True)
+    t_gen = time.perf_counter()
+    wl = synth.make(spec, device=dev)
+    torch.cuda.synchronize()
+    print(f"[bench] generated in {time.perf_counter() - t_gen:.1f} s",
+          file=sys.stderr, flush=True)
+    R, L, H = spec.requests, spec.layers, spec.kv_heads
+    U = R * L * H
+    k, n = spec.keep, spec.n_tokens
+    dt = Z.ZP_BF16 if spec.dtype == "bf16" else Z.ZP_F32
+    params = Z.make_params(spec.n_max, spec.window, spec.q_heads, dt)
+    pool = Z.make_pool(wl.k_pool, wl.v_pool)
+    tables = torch.from_numpy(wl.tables).to(dev)
+    batch = Z.DeviceBatch(
+        slot=torch.from_numpy(wl.slots).to(dev),
+        n_tokens=torch.from_numpy(wl.n_tokens).to(dev),
+        src_table=tables, dst_table=tables.clone(),
+        n_pinned=torch.zeros(R, dtype=torch.int32, device=dev),
+        num_slots=R, n_cap=wl.n_cap)
+    out = Z.alloc_outputs(U, k, wl.n_cap, dev)
+    ws = Z.alloc_workspace(pool, params, R, dev)
+    steps, warm = args.steps, args.warmup
+    holes = torch.empty((warm + steps, U), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        out.first_hole = holes[i]
+        Z.zp_compress(pool, batch, wl.q_window, wl.global_scores, params, out,
+                      ws, stream)
+        Z.zp_update_global(wl.global_scores, pool, batch, out, params, stream)
+
+    for i in range(warm):
+        step(i)
+    torch.cuda.synchronize()
+    if Z.zp_workspace_error(ws) != Z.ZP_OK:
+        raise RuntimeError("device error during warm-up")
+    Z.timing_read()  # drop anything recorded before
+    Z.timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(warm, warm + steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    Z.timing_enable(False)
+    kern = Z.timing_read()
+    if Z.zp_workspace_error(ws) != Z.ZP_OK:
+        raise RuntimeError("device error during the timed steps")
+    print(f"[bench] {steps} steps in {elapsed:.3f} s", file=sys.stderr, flush=True)
+
+    hole_np = holes[warm:].cpu().numpy().astype(np.int64)
+    M = (k - hole_np).clip(min=0)                      # moved rows per unit
+    per_step = [unit_bytes(spec, M[i]) for i in range(steps)]
+    alg = {key: float(np.mean([p[key] for p in per_step])) for key in per_step[0]}
+    ms_step = elapsed * 1e3 / steps
+    tokens_step = float(np.sum(wl.n_tokens))
+    value = tokens_step * steps / elapsed
+    gbps = alg["step"] / (ms_step * 1e-3) / 1e9
+
+    kernels = {}
+    for name, (cnt, tot) in kern.items():
+        if cnt == 0:
+            continue
+        avg = tot / cnt
+        b = alg.get(name)
+        kernels[name] = {"launches": cnt, "avg_ms": round(avg, 4),
+                         "alg_GBps": round(b / (avg * 1e-3) / 1e9, 1) if b else None}
+    dom = max(kernels, key=lambda x: kernels[x]["avg_ms"] * kernels[x]["launches"])
+    dom_ach = kernels[dom]["alg_GBps"]
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": dom_ach,
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(dom_ach / HBM_PEAK_GBPS, 4), "traffic": None}
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": steps, "warmup": warm,
+        "ms_per_step": round(ms_step, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": spec.dtype,
+        "data": "synthetic",
+        "config": {"workload": spec.name, "requests": R, "layers": L,
+                   "kv_heads": H, "q_heads": spec.q_heads,
+                   "head_dim": spec.head_dim, "block_size": spec.block_size,
+                   "n_max": spec.n_max, "tokens_per_request": n,
+                   "keep": k, "window": spec.window, "units": U,
+                   "parallelism": "single GPU"},
+        "achieved_GBps": round(gbps, 1),
+        "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+        "moved_rows_mean": round(float(M.mean()), 1),
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+    if not args.no_cpu:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(spec, wl, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,284 @@
+/*
+ * zipage.h -- C ABI of the MI355X (gfx950) Compressed-PagedAttention
+ * compression library.
+ *
+ * The operation is one KV-cache compression step of Zipage (arXiv 2603.08743,
+ * "Zipage: Maintain High Request Concurrency for LLM Reasoning through
+ * Compressed PagedAttention"), as described by the summary pages cited below:
+ *   [zh] gist.science/zh/paper/2603.08743, technical summary
+ *   [de] gist.science/de/paper/2603.08743, technical summary
+ *   [es] gist.science/es/paper/2603.08743, technical summary
+ *   [fr] gist.science/fr/paper/2603.08743, technical summary
+ *
+ * Conventions for every call:
+ *   - All pointers named "device" point to GPU memory owned by the caller; the
+ *     library never allocates, frees or synchronises device memory or streams
+ *     (the one exception, zp_workspace_error, is documented as synchronous).
+ *   - `stream` is a hipStream_t passed as void*; NULL is the null stream.
+ *     Work is enqueued asynchronously; pointers must stay valid until it ends.
+ *   - Every argument check runs before anything is enqueued. On an error
+ *     status nothing was enqueued and no output was touched. The message of
+ *     the last error on the calling thread is returned by zp_last_error().
+ *   - Device tables are checked by the kernels as they read them: a block id
+ *     outside [0, num_blocks), a token count outside its allowed range or a
+ *     slot outside [0, num_slots) makes the affected (request, layer, head)
+ *     unit skip all memory writes and records ZP_EDEVICE in the workspace.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef ZIPAGE_H
+#define ZIPAGE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t zp_status;
+
+#define ZP_OK            0
+#define ZP_EINVAL       -1  /* bad shape, pointer, alignment or value        */
+#define ZP_EUNSUPPORTED -2  /* valid but not built: head_dim, block size ... */
+#define ZP_EWORKSPACE   -3  /* workspace missing or too small                */
+#define ZP_ENOSPACE     -4  /* free list exhausted (no state was changed)    */
+#define ZP_EHIP         -5  /* the HIP runtime reported an error             */
+#define ZP_EDEVICE      -6  /* a kernel found a bad device table entry       */
+
+/* element types */
+#define ZP_F32  0
+#define ZP_BF16 1
+
+/* zp_params.flags */
+#define ZP_NONCAUSAL      (1u << 0) /* window rows see all n tokens           */
+#define ZP_PROTECT_WINDOW (1u << 1) /* the last w tokens are always kept      */
+
+/* A paged KV pool: k and v are device arrays laid out
+ * [layers][num_blocks][kv_heads][block_size][head_dim] of `dtype`, 16-byte
+ * aligned. A block id names the same block in every layer and head, so one
+ * block table serves a request in all layers ([zh] §2: the method builds on
+ * PagedAttention's block tables). */
+typedef struct {
+  void*   k;
+  void*   v;
+  int32_t num_blocks;
+  int32_t layers;
+  int32_t kv_heads;
+  int32_t block_size;   /* b; this build supports 16                        */
+  int32_t head_dim;     /* d; this build supports 64 and 128                */
+  int32_t dtype;        /* ZP_F32 or ZP_BF16                                */
+} zp_kv_pool;
+
+/* Parameters of one compression call.
+ *   n_max    -- N_max, the per-request block cap; a request compresses when
+ *               it holds N_max full blocks and keeps k = (N_max-1)*b tokens
+ *               in its first N_max-1 blocks ([zh] §2.1, [de] §2).
+ *   window   -- w, the number of most recent query states used to score
+ *               ([zh] §2.1, [de] §2, [es] §2).
+ *   q_heads  -- query heads; must be a multiple of kv_heads. Query head
+ *               h*G+g (G = q_heads/kv_heads) reads KV head h.
+ *   q_dtype  -- element type of the query windows (ZP_F32 or ZP_BF16).
+ *   w_attn, w_global, w_red -- score s = w_attn*attn + w_global*global
+ *               - w_red*red (the pages name the three parts, [zh] §2.1,
+ *               without a formula; 1, 0.5, 0.5 is the documented default).
+ *   sm_scale -- softmax scale; <= 0 selects 1/sqrt(head_dim).
+ *   flags    -- ZP_NONCAUSAL, ZP_PROTECT_WINDOW. */
+typedef struct {
+  int32_t  n_max;
+  int32_t  window;
+  int32_t  q_heads;
+  int32_t  q_dtype;
+  float    w_attn;
+  float    w_global;
+  float    w_red;
+  float    sm_scale;
+  uint32_t flags;
+} zp_params;
+
+/* The requests of one compression call (R = num_reqs). Device arrays:
+ *   slot[R]        -- query-slot row of each request: selects its window in
+ *                     q_window and its row of global scores ([zh] §2.2: only
+ *                     requests holding a query slot are compressed).
+ *   n_tokens[R]    -- tokens held, n; must satisfy n_max*b <= n <= n_cap and
+ *                     ceil(n/b) <= max_blocks (n > n_max*b: prefill overshoot).
+ *   src_table[R][max_blocks] -- current block table (logical -> physical).
+ *   dst_table[R][n_max]      -- block table after compression. For a request
+ *                     with n_pinned == 0 it must equal src_table's first n_max
+ *                     entries (in-place compaction). With n_pinned == S > 0,
+ *                     entries [0,S) equal the shared blocks, entries
+ *                     [S, n_max-1) are fresh target blocks that alias no
+ *                     source block, entry n_max-1 is any block (the new tail).
+ *   n_pinned[R]    -- S, the leading shared blocks, kept whole and never
+ *                     written ([zh] §2.2, [de] §2, [fr] §2.C).
+ * Host fields: num_reqs, max_blocks, num_slots (rows of q_window and of
+ * global_scores) and n_cap (length of a global-score row and of the attn /
+ * red / score output rows; n_cap <= 16384). */
+typedef struct {
+  int32_t        num_reqs;
+  int32_t        max_blocks;
+  int32_t        num_slots;
+  int32_t        n_cap;
+  const int32_t* slot;
+  const int32_t* n_tokens;
+  const int32_t* src_table;
+  const int32_t* dst_table;
+  const int32_t* n_pinned;
+} zp_batch;
+
+/* Outputs of zp_compress, one row per unit u = (r*layers + l)*kv_heads + h.
+ *   keep_idx[U][k]  (required) kept logical positions, ascending.
+ *   attn[U][n_cap]  (required) window attention of every token, entries
+ *                   [0, n) written; consumed by zp_update_global.
+ *   red[U][n_cap]   (optional, NULL) lightning redundancy.
+ *   score[U][n_cap] (optional, NULL) combined score, +inf where pinned.
+ *   first_hole[U]   (optional, NULL) first evicted position h. */
+typedef struct {
+  int32_t* keep_idx;
+  float*   attn;
+  float*   red;
+  float*   score;
+  int32_t* first_hole;
+} zp_compress_out;
+
+/* Bytes of device workspace zp_compress needs for num_reqs requests.
+ * Errors: ZP_EINVAL for a NULL argument or non-positive sizes. */
+zp_status zp_compress_workspace_bytes(const zp_kv_pool* pool,
+                                      const zp_params* params,
+                                      int32_t num_reqs, size_t* bytes);
+
+/* One compression step for every (request, layer, KV head) unit of `batch`
+ * ([zh] §2.1, [de] §2, [es] §2, [fr] §2.A; kernels: [zh] §2.3):
+ *   1. attn_t: mean over the w*G window rows of softmax(q.k*scale)_t, causal
+ *      by default (window row i sits at position n-w+i);
+ *   2. red_t: mean cosine similarity of k_t to the other keys of its block
+ *      (lightning redundancy, O(N b^2) for N blocks: [zh] §2.1, [fr] §2.E);
+ *   3. s_t = w_attn*attn_t + w_global*global_t - w_red*red_t, +inf for
+ *      pinned tokens (shared prefix; the window with ZP_PROTECT_WINDOW);
+ *   4. keep the k = (N_max-1)*b best tokens (higher s first, then lower
+ *      position) and write them ascending to keep_idx;
+ *   5. move kept K and V rows, in order, to logical rows [0, k) through
+ *      dst_table: in place for n_pinned == 0, into the target blocks
+ *      otherwise; shared blocks are never written ([zh] §2.2).
+ * q_window: device [num_slots][layers][w][q_heads][head_dim] of q_dtype.
+ * global_scores: device [num_slots][layers][kv_heads][n_cap] fp32 (read only
+ * here; see zp_update_global). workspace: device, 256-byte aligned, at least
+ * zp_compress_workspace_bytes; it also receives the device error word.
+ * Errors: ZP_EINVAL, ZP_EUNSUPPORTED (head_dim not 64/128, block_size not 16,
+ * w*G > 256, n_cap > 16384), ZP_EWORKSPACE, ZP_EHIP. */
+zp_status zp_compress(const zp_kv_pool* pool, const zp_batch* batch,
+                      const void* q_window, const float* global_scores,
+                      const zp_params* params, const zp_compress_out* out,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Global-score update after zp_compress on the same stream ([zh] §2.1 global
+ * score from past attention; update kernel [zh] §2.3): for every unit,
+ * g'_t = g_{keep[t]} + attn_{keep[t]} for t < k and g'_t = 0 for
+ * t in [k, n_cap), in place in global_scores (the row of slot[r]).
+ * Errors: ZP_EINVAL, ZP_EUNSUPPORTED, ZP_EHIP. */
+zp_status zp_update_global(float* global_scores, const zp_kv_pool* pool,
+                           const zp_batch* batch, const zp_compress_out* out,
+                           const zp_params* params, void* stream);
+
+/* Reads the device error word of a workspace after the caller's stream work
+ * has finished: synchronises `stream`, stores ZP_OK or ZP_EDEVICE in *code
+ * and clears the word. Errors: ZP_EINVAL, ZP_EHIP. */
+zp_status zp_workspace_error(void* workspace, void* stream, int32_t* code);
+
+/* Decode attention over a paged cache, the consumer of the compressed blocks
+ * ([zh] §2.3: decoding runs PagedAttention over the blocks):
+ * out[r][l][hq][:] = softmax(q[r][l][hq] . K^T * scale) V over the seq_lens[r]
+ * tokens of request r, with K, V read through block_tables.
+ * out: device fp32 [num_reqs][layers][q_heads][head_dim]; q: device
+ * [num_reqs][layers][q_heads][head_dim] of params->q_dtype; block_tables:
+ * device [num_reqs][max_blocks]; seq_lens: device [num_reqs], 1 <= len <=
+ * max_blocks*b. Only params->q_heads, q_dtype and sm_scale are read.
+ * Errors: ZP_EINVAL, ZP_EUNSUPPORTED, ZP_EHIP. */
+zp_status zp_paged_decode(float* out, const void* q, const zp_kv_pool* pool,
+                          const int32_t* block_tables, int32_t max_blocks,
+                          const int32_t* seq_lens, int32_t num_reqs,
+                          const zp_params* params, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Host-side block bookkeeping (no GPU calls). A block manager owns the free
+ * list and the reference counts of a pool of num_blocks blocks. The free list
+ * is a LIFO stack; a fresh manager pops id 0 first. Not thread-safe: the
+ * caller serialises calls on one manager.
+ * ------------------------------------------------------------------------ */
+typedef struct zp_bm zp_bm;
+typedef struct zp_plan zp_plan;
+
+/* NULL on a bad size or out of memory. */
+zp_bm* zp_bm_create(int32_t num_blocks);
+void zp_bm_destroy(zp_bm* bm);
+
+/* Pops n blocks into ids[n] (refcount 1 each). ZP_ENOSPACE leaves the
+ * manager unchanged. */
+zp_status zp_bm_alloc(zp_bm* bm, int32_t n, int32_t* ids);
+/* One more user of a held block (a shared prefix, [de] §2). */
+zp_status zp_bm_incref(zp_bm* bm, int32_t id);
+/* One user fewer for each id; blocks reaching 0 are pushed in array order. */
+zp_status zp_bm_release(zp_bm* bm, int32_t n, const int32_t* ids);
+int32_t zp_bm_free_count(const zp_bm* bm);
+/* -1 for an id out of range. */
+int32_t zp_bm_refcount(const zp_bm* bm, int32_t id);
+/* Copies the free stack bottom to top into ids (at most cap); returns the
+ * number of free blocks. */
+int32_t zp_bm_free_list(const zp_bm* bm, int32_t* ids, int32_t cap);
+
+/* Plans one compression call ([zh] §2.1 trigger; [zh] §2.2 shared prefix):
+ * host_tables[R][max_blocks], n_tokens[R] on the host. For every request,
+ * S = the leading run of blocks with refcount > 1 (at most n_max-1).
+ *   S == 0: dst_tables[r] = its first n_max blocks (in place);
+ *   S  > 0: dst_tables[r] = [shared 0..S-1, n_max-1-S targets popped now in
+ *           logical order, old block n_max-1 as the tail].
+ * Blocks that compression frees (old private blocks S..n_max-2 when S > 0,
+ * then every block past n_max) are recorded in the plan, in logical order,
+ * and pushed only by zp_bm_commit. Outputs dst_tables[R][n_max] and
+ * n_pinned[R] (= S) on the host. Errors: ZP_EINVAL (bad sizes, n_tokens
+ * below n_max*b, a block id out of range), ZP_ENOSPACE (not enough free
+ * blocks for the targets: nothing changed). */
+zp_status zp_bm_plan_compress(zp_bm* bm, int32_t num_reqs,
+                              const int32_t* host_tables, int32_t max_blocks,
+                              const int32_t* n_tokens, int32_t n_max,
+                              int32_t block_size, int32_t* dst_tables,
+                              int32_t* n_pinned, zp_plan** plan);
+/* After the compression stream's work has finished (an event the caller
+ * waited on): targets keep refcount 1, freed blocks get 0 and are pushed in
+ * plan order, shared counts are unchanged. Consumes the plan. */
+zp_status zp_bm_commit(zp_bm* bm, zp_plan* plan);
+/* Abandons a plan: its targets go back on the stack (reverse pop order), so
+ * the manager is as before the plan. Consumes the plan. */
+zp_status zp_bm_abort(zp_bm* bm, zp_plan* plan);
+/* Blocks the plan will free, in push order; returns their number (copies at
+ * most cap into ids). */
+int32_t zp_plan_freed(const zp_plan* plan, int32_t* ids, int32_t cap);
+/* Targets the plan popped, in pop order; returns their number. */
+int32_t zp_plan_targets(const zp_plan* plan, int32_t* ids, int32_t cap);
+
+/* ---------------------------------------------------------------------------
+ * Kernel timing for measurement: while enabled, zp_compress,
+ * zp_update_global and zp_paged_decode record a pair of HIP events around
+ * every kernel they launch, on the launch stream. zp_timing_read waits for
+ * the recorded events, and returns per kernel kind the launch count and the
+ * summed milliseconds, then clears the record.
+ * ------------------------------------------------------------------------ */
+#define ZP_KERNEL_SCORE   0   /* score + select                              */
+#define ZP_KERNEL_COMPACT 1   /* K/V row compaction                          */
+#define ZP_KERNEL_GLOBAL  2   /* global-score update                         */
+#define ZP_KERNEL_DECODE  3   /* paged decode                                */
+#define ZP_KERNEL_KINDS   4
+
+zp_status zp_timing_enable(int32_t enable);
+zp_status zp_timing_read(int32_t* launches /*[ZP_KERNEL_KINDS]*/,
+                         double* total_ms /*[ZP_KERNEL_KINDS]*/);
+
+/* Text of a status code; message of the last error on this thread. */
+const char* zp_status_str(zp_status status);
+const char* zp_last_error(void);
+/* Library version string. */
+const char* zp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ZIPAGE_H */

@@ -1,0 +1,53 @@
+// Internal host helpers shared by the library's C++ files: thread-local error
+// messages and the launchers each kernel file exports.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "zipage.h"
+
+namespace zp {
+
+// Stores a printf-style message as this thread's last error.
+void set_error(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
+// set_error + return code.
+zp_status fail(zp_status code, const char* fmt, ...)
+    __attribute__((format(printf, 2, 3)));
+
+// Geometry every kernel of one compression call shares (all sizes checked).
+struct CompressGeom {
+  int32_t R, L, Hkv, Hq, G, d, b, n_max, k, w, wG, n_cap, num_blocks;
+  int32_t max_blocks, num_slots;
+  int32_t dtype, q_dtype;
+  uint32_t flags;
+  float w_attn, w_global, w_red, scale_log2;
+};
+
+// Launchers (defined next to their kernels). Each returns ZP_OK or ZP_EHIP
+// (launch error), after recording the error text.
+zp_status launch_score_select(const CompressGeom& g, const zp_kv_pool& pool,
+                              const zp_batch& batch, const void* q_window,
+                              const float* global_scores,
+                              const zp_compress_out& out, int32_t* hole,
+                              int32_t* err, void* stream);
+zp_status launch_compact(const CompressGeom& g, const zp_kv_pool& pool,
+                         const zp_batch& batch, const int32_t* keep,
+                         const int32_t* hole, int32_t* err, void* stream);
+zp_status launch_global(const CompressGeom& g, float* global_scores,
+                        const zp_batch& batch, const int32_t* keep,
+                        const float* attn, void* stream);
+
+struct DecodeGeom {
+  int32_t R, L, Hkv, Hq, G, d, b, num_blocks, max_blocks, dtype, q_dtype;
+  float scale_log2;
+};
+zp_status launch_decode(const DecodeGeom& g, float* out, const void* q,
+                        const zp_kv_pool& pool, const int32_t* tables,
+                        const int32_t* seq_lens, void* stream);
+
+// Timing hooks: record an event pair around kernel `kind` when enabled.
+void timing_before(int kind, void* stream);
+void timing_after(int kind, void* stream);
+
+}  // namespace zp

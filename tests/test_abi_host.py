@@ -1,0 +1,220 @@
+"""Host-side checks of the C ABI that need no GPU.
+
+* libzipage.so loads and exports every function include/zipage.h declares;
+* the C++ block manager (zp_bm_*) matches the oracle's bookkeeping exactly on
+  random histories (pops, pushes, plans, commits, aborts);
+* argument errors are reported with the documented status before anything
+  is enqueued (so these calls never touch a device).
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle as O
+import kv_cache_compression_paged_amd as Z
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "zipage.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(zp_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = Z.lib()
+    declared = _declared()
+    assert len(declared) >= 20
+    for name in declared:
+        assert hasattr(lib, name), f"{name} not exported"
+    nm = subprocess.run(["nm", "-D", "--defined-only", Z.LIB_PATH],
+                        capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r" T (zp_\w+)", nm))
+    assert set(declared) <= exported
+    assert set(Z.EXPORTED) == set(declared)
+
+
+def test_status_strings():
+    lib = Z.lib()
+    for code, name in [(0, "ZP_OK"), (-1, "ZP_EINVAL"), (-2, "ZP_EUNSUPPORTED"),
+                       (-3, "ZP_EWORKSPACE"), (-4, "ZP_ENOSPACE"), (-5, "ZP_EHIP"),
+                       (-6, "ZP_EDEVICE")]:
+        assert lib.zp_status_str(code).decode() == name
+
+
+# ------------------------------------------------------- block manager ---
+
+def _same_state(bm, bp):
+    assert bm.free_list() == bp.stack
+    assert [bm.refcount(i) for i in range(bm.num_blocks)] == bp.refcount
+
+
+def test_block_manager_matches_oracle_random_histories():
+    rng = np.random.default_rng(123)
+    for trial in range(30):
+        nb = int(rng.integers(20, 80))
+        bm, bp = Z.BlockManager(nb), O.BlockPool(nb)
+        n_max, b = int(rng.integers(2, 6)), int(rng.choice([1, 2, 4, 16]))
+        reqs = []
+        for _ in range(int(rng.integers(1, 4))):
+            # a group sharing s leading blocks, then private blocks
+            s = int(rng.integers(0, n_max))
+            members = int(rng.integers(1, 4))
+            if bm.free_count() < s + members * (n_max - s + 2):
+                break
+            shared = bm.alloc(s)
+            assert shared == bp.alloc(s)
+            for m in range(members):
+                if m:
+                    for x in shared:
+                        bm.incref(x)
+                        bp.incref(x)
+                extra = int(rng.integers(0, 3))
+                priv = bm.alloc(n_max - s + extra)
+                assert priv == bp.alloc(n_max - s + extra)
+                ntok = (n_max + extra) * b - int(rng.integers(0, b)) * (extra > 0)
+                reqs.append((shared + priv, max(ntok, n_max * b)))
+        _same_state(bm, bp)
+        if not reqs:
+            continue
+        mb = max(len(t) for t, _ in reqs)
+        tables = np.zeros((len(reqs), mb), dtype=np.int32)
+        for i, (t, _) in enumerate(reqs):
+            tables[i, :len(t)] = t
+        ntoks = [n for _, n in reqs]
+        try:
+            oplan = bp.plan_compress([list(t) for t in tables], ntoks, n_max, b)
+        except MemoryError:
+            with pytest.raises(Z.ZipageError) as ei:
+                bm.plan_compress(tables, ntoks, n_max, b)
+            assert ei.value.status == Z.ZP_ENOSPACE
+            _same_state(bm, bp)
+            continue
+        plan = bm.plan_compress(tables, ntoks, n_max, b)
+        assert plan.dst_tables.tolist() == [list(x) for x in oplan.dst_tables]
+        assert plan.n_pinned.tolist() == list(oplan.n_pinned)
+        assert plan.targets() == oplan.popped
+        assert plan.freed() == oplan.to_free
+        if rng.random() < 0.3:
+            bm.abort(plan)
+            bp.stack.extend(reversed(oplan.popped))
+        else:
+            bm.commit(plan)
+            bp.commit(oplan)
+        _same_state(bm, bp)
+        # conservation: every block is either free or held, exactly once
+        free = bm.free_list()
+        held = [i for i in range(nb) if bm.refcount(i) > 0]
+        assert sorted(free + held) == list(range(nb))
+
+
+def test_block_manager_errors_change_nothing():
+    bm = Z.BlockManager(6)
+    ids = bm.alloc(4)
+    with pytest.raises(Z.ZipageError) as ei:
+        bm.alloc(3)
+    assert ei.value.status == Z.ZP_ENOSPACE
+    assert bm.free_count() == 2
+    with pytest.raises(Z.ZipageError):
+        bm.incref(5)                      # free block
+    with pytest.raises(Z.ZipageError):
+        bm.release([ids[0], ids[0]])      # released twice: nothing changes
+    assert bm.refcount(ids[0]) == 1
+    with pytest.raises(Z.ZipageError):
+        bm.plan_compress(np.array([ids]), [3], 4, 1)   # below trigger
+    with pytest.raises(Z.ZipageError):
+        bm.plan_compress(np.array([[0, 1, 2, 99]]), [4], 4, 1)  # bad id
+    bm.release(ids)
+    assert bm.free_count() == 6
+
+
+# ------------------------------------------------ argument validation ---
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+def _pool(**kw):
+    d = dict(k=FAKE, v=FAKE, num_blocks=64, layers=2, kv_heads=2, block_size=16,
+             head_dim=128, dtype=Z.ZP_BF16)
+    d.update(kw)
+    return Z.KVPool(**d)
+
+
+def _params(**kw):
+    d = dict(n_max=4, window=8, q_heads=8, q_dtype=Z.ZP_BF16, w_attn=1.0,
+             w_global=0.5, w_red=0.5, sm_scale=0.0, flags=0)
+    d.update(kw)
+    return Z.Params(**d)
+
+
+def _batch(**kw):
+    d = dict(num_reqs=2, max_blocks=4, num_slots=2, n_cap=64, slot=FAKE,
+             n_tokens=FAKE, src_table=FAKE, dst_table=FAKE, n_pinned=FAKE)
+    d.update(kw)
+    return Z.BatchStruct(**d)
+
+
+def _compress(pool=None, batch=None, params=None, ws_bytes=1 << 20,
+              q=FAKE, keep=FAKE, attn=FAKE, ws=0x100000):
+    out = Z.CompressOut(keep, attn, None, None, None)
+    return Z.lib().zp_compress(ctypes.byref(pool or _pool()),
+                               ctypes.byref(batch or _batch()), q, FAKE,
+                               ctypes.byref(params or _params()),
+                               ctypes.byref(out), ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(pool=_pool(block_size=8)), Z.ZP_EUNSUPPORTED),
+    (dict(pool=_pool(head_dim=96)), Z.ZP_EUNSUPPORTED),
+    (dict(pool=_pool(dtype=7)), Z.ZP_EINVAL),
+    (dict(pool=_pool(k=FAKE + 4)), Z.ZP_EINVAL),
+    (dict(params=_params(q_heads=7)), Z.ZP_EINVAL),
+    (dict(params=_params(q_dtype=Z.ZP_F32)), Z.ZP_EUNSUPPORTED),
+    (dict(params=_params(n_max=1)), Z.ZP_EINVAL),
+    (dict(params=_params(window=0)), Z.ZP_EINVAL),
+    (dict(params=_params(flags=8)), Z.ZP_EINVAL),
+    (dict(params=_params(window=49, flags=Z.ZP_PROTECT_WINDOW)), Z.ZP_EINVAL),
+    (dict(params=_params(w_red=float("nan"))), Z.ZP_EINVAL),
+    (dict(params=_params(window=64, q_heads=8)), Z.ZP_EUNSUPPORTED),  # w*G=256
+    (dict(batch=_batch(max_blocks=3)), Z.ZP_EINVAL),
+    (dict(batch=_batch(n_cap=32)), Z.ZP_EINVAL),
+    (dict(batch=_batch(n_cap=20000)), Z.ZP_EUNSUPPORTED),
+    (dict(batch=_batch(n_pinned=None)), Z.ZP_EINVAL),
+    (dict(q=None), Z.ZP_EINVAL),
+    (dict(keep=None), Z.ZP_EINVAL),
+    (dict(ws_bytes=16), Z.ZP_EWORKSPACE),
+    (dict(ws=0x100010), Z.ZP_EWORKSPACE),
+])
+def test_compress_rejects_bad_arguments_before_enqueue(kw, status):
+    assert _compress(**kw) == status
+    assert Z.last_error()
+
+
+def test_compress_empty_batch_is_a_no_op():
+    assert _compress(batch=_batch(num_reqs=0)) == Z.ZP_OK
+
+
+def test_workspace_size_formula():
+    assert Z.zp_compress_workspace_bytes(_pool(), _params(), 2) == 256 + 256
+    assert Z.zp_compress_workspace_bytes(_pool(), _params(), 100) == \
+        256 + (100 * 2 * 2 * 4 + 255) // 256 * 256
+
+
+def test_decode_rejects_bad_arguments():
+    lib = Z.lib()
+    r = lib.zp_paged_decode(FAKE, FAKE, ctypes.byref(_pool(head_dim=80)), FAKE,
+                            4, FAKE, 2, ctypes.byref(_params()), None)
+    assert r == Z.ZP_EUNSUPPORTED
+    r = lib.zp_paged_decode(FAKE, FAKE, ctypes.byref(_pool()), FAKE, 4, FAKE, 2,
+                            ctypes.byref(_params(q_heads=3)), None)
+    assert r == Z.ZP_EINVAL
+    r = lib.zp_paged_decode(FAKE, FAKE, ctypes.byref(_pool()), FAKE, 4, FAKE, 0,
+                            ctypes.byref(_params()), None)
+    assert r == Z.ZP_OK

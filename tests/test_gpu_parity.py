@@ -1,0 +1,232 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Small cases compare every unit element by element (see tests/parity.py for
+the rules); the full-size cases run the exact launch configuration bench.py
+times and compare a seeded sample of units one by one, plus properties that
+hold for every unit.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import kv_cache_compression_paged_amd as Z
+from kv_cache_compression_paged_amd import synth
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _check(case, label):
+    _say(f"[parity] {label}: {case.spec}")
+    res = P.run_case(case)
+    _say(f"[parity] {label}: ok={res.ok} stats={res.stats}")
+    assert res.ok, "\n".join(res.failures)
+
+
+# ---------------------------------------------------------------- small ---
+
+SMALL_MODEL = synth.scaled(synth.SMALL, requests=2, layers=2, n_max=16,
+                           pool_blocks=48)
+EIGHT_B = synth.scaled(synth.EIGHT_B, requests=3, layers=2, kv_heads=2,
+                       q_heads=8, n_max=32, pool_blocks=112)
+PREFIX = synth.scaled(synth.PREFIX, requests=4, layers=2, kv_heads=2,
+                      q_heads=8, n_max=12, groups=2, shared_blocks=3,
+                      pool_blocks=6 + 4 * 9 + 4 * 8 + 5)
+D64 = synth.scaled(synth.EIGHT_B, requests=2, layers=1, kv_heads=2, q_heads=4,
+                   head_dim=64, n_max=20, window=16, pool_blocks=48,
+                   near_dup=False)
+F32_D128 = synth.scaled(synth.TINY, requests=2, layers=1, kv_heads=1,
+                        q_heads=2, head_dim=128, n_max=10, window=16,
+                        pool_blocks=24, permute=True)
+
+
+def test_tiny_fp32_full_config():
+    _check(P.Case(synth.TINY), "tiny fp32 (d=64, G=2, w=8)")
+
+
+def test_small_model_shape():
+    _check(P.Case(SMALL_MODEL), "G=6, w=32 (192 window rows)")
+
+
+def test_8b_shape_near_duplicates():
+    _check(P.Case(EIGHT_B), "G=4, w=32, near-duplicate keys")
+
+
+def test_noncausal():
+    _check(P.Case(EIGHT_B, flags=Z.ZP_NONCAUSAL), "non-causal window")
+
+
+def test_protect_window():
+    _check(P.Case(EIGHT_B, flags=Z.ZP_PROTECT_WINDOW), "protected window")
+
+
+def test_bf16_head_dim_64():
+    _check(P.Case(D64), "bf16 d=64")
+
+
+def test_fp32_head_dim_128():
+    _check(P.Case(F32_D128), "fp32 d=128")
+
+
+def test_prefill_overshoot_ragged_tail():
+    spec = synth.scaled(EIGHT_B, requests=3, pool_blocks=112 + 12)
+    n = spec.n_tokens
+    _check(P.Case(spec, n_tokens=[n + 5, n + 16, n + 37], max_blocks=spec.n_max + 3),
+           "overshoot n = N+5, N+16, N+37 (E > b, ragged last block)")
+
+
+def test_prefix_targets_with_block_manager():
+    _check(P.Case(PREFIX, use_block_manager=True),
+           "shared prefix -> target blocks (plans from zp_bm)")
+
+
+def _forced_global(spec, evict_positions):
+    g = np.zeros((spec.requests, spec.layers, spec.kv_heads, spec.n_tokens))
+    g[..., list(evict_positions)] = -100.0
+    return g
+
+
+@pytest.mark.parametrize("name,positions", [
+    ("evict block 0 (every row shifts)", list(range(16))),
+    ("evict the last block (nothing moves)", None),
+    ("alternating holes", "alt"),
+])
+def test_adversarial_keep_sets(name, positions):
+    spec = synth.scaled(EIGHT_B, requests=2)
+    n = spec.n_tokens
+    if positions is None:
+        positions = list(range(n - 16, n))
+    elif positions == "alt":
+        positions = [17 * i + 3 for i in range(16)]
+    _check(P.Case(spec, global_override=_forced_global(spec, positions)), name)
+
+
+def test_forced_ties_keep_prefix():
+    spec = synth.scaled(EIGHT_B, requests=1, layers=1)
+    g = np.full((1, 1, spec.kv_heads, spec.n_tokens), 0.25)
+    case = P.Case(spec, flags=Z.ZP_NONCAUSAL, identical_keys=True,
+                  global_override=g)
+    res = P.run_case(case)
+    assert res.ok, "\n".join(res.failures)
+
+
+# ------------------------------------------------------------ full size ---
+
+def _full_size_sampled(spec, n_samples, seed):
+    """Run the full call and check sampled units against the oracle."""
+    dev = "cuda"
+    _say(f"[full] generating {spec.name}")
+    wl = synth.make(spec, device=dev)
+    R, L, H, b = spec.requests, spec.layers, spec.kv_heads, spec.block_size
+    U = R * L * H
+    k, n = spec.keep, spec.n_tokens
+    rng = np.random.default_rng(seed)
+    units = sorted(set(int(x) for x in rng.choice(U, size=n_samples, replace=False)))
+    units = sorted(set(units) | {0, U - 1})
+    G = spec.q_heads // H
+    tables = wl.tables
+    if spec.shared_blocks:
+        bm = Z.BlockManager(spec.pool_blocks)
+        bm.alloc(spec.pool_blocks)
+        for bid in range(spec.pool_blocks):
+            c = int(wl.refcount[bid])
+            if c == 0:
+                bm.release([bid])
+            for _ in range(c - 1):
+                bm.incref(bid)
+        plan = bm.plan_compress(tables, wl.n_tokens, spec.n_max, b)
+        dst, pinned = plan.dst_tables, plan.n_pinned
+    else:
+        dst, pinned = tables.copy(), np.zeros(R, dtype=np.int32)
+    tab_dev = torch.from_numpy(tables).to(dev)
+    saved = {}
+    for u in units:
+        r, l, h = u // (L * H), (u // H) % L, u % H
+        blocks = tab_dev[r].long()
+        kr = wl.k_pool[l, blocks, h].reshape(n, -1)
+        vr = wl.v_pool[l, blocks, h].reshape(n, -1)
+        saved[u] = (synth.raw_numpy(kr), synth.raw_numpy(vr),
+                    synth.raw_numpy(wl.q_window[r, l, :, h * G:(h + 1) * G]),
+                    wl.global_scores[r, l, h].cpu().numpy().copy())
+    zparams, oparams = P._params_for(spec, 0)
+    pool = Z.make_pool(wl.k_pool, wl.v_pool)
+    batch = Z.DeviceBatch(
+        slot=torch.from_numpy(wl.slots).to(dev),
+        n_tokens=torch.from_numpy(wl.n_tokens).to(dev),
+        src_table=tab_dev,
+        dst_table=torch.from_numpy(np.ascontiguousarray(dst, dtype=np.int32)).to(dev),
+        n_pinned=torch.from_numpy(np.ascontiguousarray(pinned, dtype=np.int32)).to(dev),
+        num_slots=R, n_cap=wl.n_cap)
+    out = Z.alloc_outputs(U, k, wl.n_cap, dev, debug=True)
+    ws = Z.alloc_workspace(pool, zparams, R, dev)
+    _say(f"[full] compress {spec.name}: U={U}")
+    Z.zp_compress(pool, batch, wl.q_window, wl.global_scores, zparams, out, ws)
+    Z.zp_update_global(wl.global_scores, pool, batch, out, zparams)
+    torch.cuda.synchronize()
+    assert Z.zp_workspace_error(ws) == Z.ZP_OK
+    # properties of every unit
+    keep = out.keep_idx
+    assert bool((keep[:, 1:] > keep[:, :-1]).all()), "keep rows not ascending"
+    assert int(keep.min()) >= 0 and int(keep.max()) < n
+    if not spec.shared_blocks:
+        ar = torch.arange(k, device=dev, dtype=torch.int32)
+        hole_ref = torch.where(keep != ar, ar, torch.full_like(ar, k)).min(dim=1).values
+        assert torch.equal(hole_ref, out.first_hole)
+    else:
+        assert bool((keep[:, :spec.shared_blocks * b] ==
+                     torch.arange(spec.shared_blocks * b, device=dev,
+                                  dtype=torch.int32)).all())
+    tail = wl.global_scores[..., k:]
+    assert bool((tail == 0).all()), "global tail not zeroed"
+    dst_dev = batch.dst_table
+    for u in units:
+        r, l, h = u // (L * H), (u // H) % L, u % H
+        kr, vr, q, g = saved[u]
+        keys = O.widen(kr, spec.dtype)
+        ur = O.score_unit(O.widen(q, spec.dtype), keys, g.astype(np.float64), n,
+                          int(pinned[r]), oparams)
+        ga = out.attn[u, :n].cpu().numpy().astype(np.float64)
+        gr = out.red[u, :n].cpu().numpy().astype(np.float64)
+        gs = out.score[u, :n].cpu().numpy()
+        assert np.all(np.abs(ga - ur.attn) <= P.ATTN_RTOL * np.abs(ur.attn) + P.ATTN_ATOL)
+        assert np.all(np.abs(gr - ur.red) <= P.RED_RTOL * np.abs(ur.red) + P.RED_ATOL)
+        fin = np.isfinite(ur.score)
+        assert np.array_equal(fin, np.isfinite(gs))
+        assert np.all(np.abs(gs[fin] - ur.score[fin]) <=
+                      P.SCORE_RTOL * np.abs(ur.score[fin]) + P.SCORE_ATOL)
+        gk = keep[u].cpu().numpy()
+        assert np.array_equal(gk, O.select_keep(gs.astype(np.float64), k, ~fin))
+        diff = set(gk.tolist()) ^ set(ur.keep.tolist())
+        tau = min(float(ur.score[t]) for t in ur.keep if fin[t])
+        assert all(abs(ur.score[t] - tau) <= P.BAND for t in diff)
+        # compacted rows: logical rows [0, k) through the destination table
+        blocks = dst_dev[r].long()
+        nk = synth.raw_numpy(wl.k_pool[l, blocks, h].reshape(spec.n_max * b, -1))
+        nv = synth.raw_numpy(wl.v_pool[l, blocks, h].reshape(spec.n_max * b, -1))
+        assert nk[:k].tobytes() == kr[gk].tobytes(), f"K rows of unit {u}"
+        assert nv[:k].tobytes() == vr[gk].tobytes(), f"V rows of unit {u}"
+        if not spec.shared_blocks:  # the tail block keeps its old rows
+            assert nk[k:].tobytes() == kr[k:n].tobytes()
+        gn = wl.global_scores[r, l, h].cpu().numpy().astype(np.float64)
+        gref = O.update_global(g, ur.attn, gk, k)
+        assert np.all(np.abs(gn - gref) <= 1e-4 * np.abs(gref) + 1e-6)
+    _say(f"[full] {spec.name}: {len(units)} sampled units match")
+    del wl, out
+    torch.cuda.empty_cache()
+
+
+def test_full_size_small_model_sampled():
+    _full_size_sampled(synth.SMALL, 6, 11)
+
+
+def test_full_size_8b_sampled():
+    _full_size_sampled(synth.EIGHT_B, 6, 12)
