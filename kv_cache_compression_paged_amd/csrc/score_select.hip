@@ -1,12 +1,13 @@
-// Score and select kernel: one workgroup (4 waves) per (request, layer, KV
+// Score and select kernel: one workgroup of 8 waves per (request, layer, KV
 // head) unit.
 //
 // Steps, in the order of the method ([zh] §2.1, [de] §2, [es] §2):
 //   phase 1  sweep the unit's keys once through the block table: window
-//            logits Q K^T on MFMA, per-row softmax statistics (max and sum,
-//            online), and the lightning redundancy of every block from the
-//            block's 16x16 key Gram matrix (also MFMA, on the same registers:
-//            intra-block similarity only, [zh] §2.1, [fr] §2.E);
+//            logits Q K^T on MFMA, per-row softmax normalisers (sums against
+//            a per-row reference, exact online fallback on overflow), and the
+//            lightning redundancy of every block from the block's 16x16 key
+//            Gram matrix (also MFMA, on the same registers: intra-block
+//            similarity only, [zh] §2.1, [fr] §2.E);
 //   phase 2  sweep the keys again, recompute the logits and sum the
 //            normalised probabilities down each column -> attn_t; combine
 //            s_t = w_attn attn_t + w_global g_t - w_red red_t (+inf if pinned);
@@ -15,23 +16,34 @@
 //            ties broken toward the lower position, then the kept positions
 //            are written ascending together with the first evicted one.
 //
-// Waves split the key blocks (wave v takes blocks v, v+4, ...); each wave
-// keeps the whole query window of the unit in registers as MFMA fragments,
-// so every key fragment is loaded once per sweep straight from HBM into the
-// B operand and used for all window rows. Phase 2 re-reads the keys: the
-// column means need every row's normaliser first.
+// Organisation (gfx950). Wave w is (key quarter kq = w % 4, row half
+// rg = w / 4): at step s the two waves of quarter kq handle key block
+// 4s + kq, each for its half of the window rows, whose MFMA A fragments
+// stay in registers for the whole unit. Key blocks reach LDS by direct
+// global->LDS loads (16 bytes per lane, 1 KiB fully coalesced per
+// instruction) into a ring of kRing slots per quarter, issued kRing-1 steps
+// ahead, so ~80 KiB per CU are in flight without costing registers; each
+// wave of the pair issues half of a block's loads. The 16-byte chunks of a
+// block row are XOR-swizzled by row in LDS, so the ds_read_b128 fragment
+// reads (lane (j, n) takes row n, chunk group j) hit distinct banks. A step
+// is fenced by an exact s_waitcnt on the wave's own loads plus a raw
+// s_barrier (a __syncthreads would drain every load in flight). Two waves
+// share a SIMD, so one's MFMA overlaps the other's exp/VALU work.
 #include <hip/hip_runtime.h>
 
 #include "zp_device.h"
 #include "zp_host.h"
+
+#define ZP_LDS __attribute__((address_space(3)))
 
 namespace {
 
 using zpd::f32x4_t;
 using zpd::Frag;
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
+constexpr int kThreads = 512;
+constexpr int kWaves = 8;
+constexpr int kQuarters = 4;
 constexpr int kB = 16;  // block size b (one key tile = one block)
 
 struct ScoreArgs {
@@ -55,26 +67,82 @@ struct ScoreArgs {
   float w_attn, w_global, w_red, sl2;  // sl2 = softmax scale * log2(e)
 };
 
+// s_waitcnt with vmcnt = n (0..28), expcnt untouched, lgkmcnt = 0.
+__device__ __forceinline__ void wait_vm_lgkm0(int n) {
+#define ZP_W(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (((N) >> 4) << 14) | (7 << 4))
+  switch (n) {
+    case 0: ZP_W(0); break;    case 1: ZP_W(1); break;    case 2: ZP_W(2); break;
+    case 3: ZP_W(3); break;    case 4: ZP_W(4); break;    case 5: ZP_W(5); break;
+    case 6: ZP_W(6); break;    case 7: ZP_W(7); break;    case 8: ZP_W(8); break;
+    case 9: ZP_W(9); break;    case 10: ZP_W(10); break;  case 11: ZP_W(11); break;
+    case 12: ZP_W(12); break;  case 13: ZP_W(13); break;  case 14: ZP_W(14); break;
+    case 15: ZP_W(15); break;  case 16: ZP_W(16); break;  case 17: ZP_W(17); break;
+    case 18: ZP_W(18); break;  case 19: ZP_W(19); break;  case 20: ZP_W(20); break;
+    case 21: ZP_W(21); break;  case 22: ZP_W(22); break;  case 23: ZP_W(23); break;
+    case 24: ZP_W(24); break;  case 25: ZP_W(25); break;  case 26: ZP_W(26); break;
+    case 27: ZP_W(27); break;  case 28: ZP_W(28); break;
+    default: ZP_W(0); break;
+  }
+#undef ZP_W
+}
+
+// Raw workgroup barrier that keeps LDS accesses in program order around it
+// without waiting for outstanding global->LDS loads.
+__device__ __forceinline__ void step_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <typename E, int D>
+struct TileGeom {
+  static constexpr int kRowBytes = D * E::kBytes;          // 128, 256 or 512
+  static constexpr int kRowChunks = kRowBytes / 16;         // 8, 16 or 32
+  static constexpr int kTileBytes = kB * kRowBytes;         // 2, 4 or 8 KiB
+  static constexpr int kLoads = kTileBytes / 1024;          // per block
+  static constexpr int kLoadsPerWave = kLoads / 2;          // per wave of a pair
+  static constexpr int kSwz = kRowChunks < 16 ? kRowChunks - 1 : 15;
+  static constexpr int kRing0 = 96 * 1024 / (kQuarters * kTileBytes);
+  static constexpr int kRing = kRing0 > 8 ? 8 : kRing0;     // slots per quarter
+  static_assert(kLoadsPerWave >= 1, "tile too small");
+  static_assert(kRing >= 3, "ring too short");
+  static_assert((kRing - 1) * kLoadsPerWave <= 28, "wait count range");
+  // LDS byte offset of chunk (row, c) inside a slot
+  __device__ static constexpr int chunk_off(int row, int c) {
+    return row * kRowBytes + ((c ^ (row & kSwz)) << 4);
+  }
+};
+
 template <typename E, int D, int RT>
 __global__ __launch_bounds__(kThreads) void score_select_kernel(ScoreArgs a) {
   using FragT = Frag<E, D>;
+  using TG = TileGeom<E, D>;
   constexpr int kRows = RT * 16;
-  extern __shared__ float s_tok[];  // [n_cap]: red, then s, then order keys
-  __shared__ float st_m[kWaves][kRows];
-  __shared__ float st_z[kWaves][kRows];
+  constexpr int RTW = (RT + 1) / 2;     // row tiles of the first row half
+  constexpr int kRing = TG::kRing;
+  __shared__ __attribute__((aligned(16))) char ring[kQuarters][kRing][TG::kTileBytes];
+  extern __shared__ float s_tok[];  // [n_cap]: red, then order keys
+  __shared__ int tab[1024];
+  __shared__ float st_m[kQuarters][kRows];
+  __shared__ float st_z[kQuarters][kRows];
   __shared__ float mprime[kRows];
   __shared__ int rowpos[kRows];
-  __shared__ int scratch[8];
-  __shared__ uint32_t hist[256];
+  __shared__ float xchg[kQuarters][2][16];
+  __shared__ int scratch[16];
+  __shared__ uint32_t hist[kWaves][257];  // one padded histogram per wave
   __shared__ int sel[2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
+  const int kq = wave & 3, rg = wave >> 2;
   const int jg = lane >> 4, nl = lane & 15;
   const int u = blockIdx.x;
   const int h = u % a.Hkv;
   const int l = (u / a.Hkv) % a.L;
   const int r = u / (a.Hkv * a.L);
+  // this wave's row tiles: [rt0, rt0 + nrt)
+  const int rt0 = rg * RTW;
+  const int nrt = rg ? RT - RTW : RTW;
 
   // ---- device-side checks of this unit's tables (no writes on failure)
   const int n = a.n_tokens[r];
@@ -83,14 +151,17 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(ScoreArgs a) {
   const bool protect = (a.flags & ZP_PROTECT_WINDOW) != 0;
   const bool causal = (a.flags & ZP_NONCAUSAL) == 0;
   bool bad = n < a.n_max * kB || n > a.n_cap || (n + kB - 1) / kB > a.max_blocks ||
-             slot < 0 || slot >= a.num_slots || S < 0 ||
+             (n + kB - 1) / kB > 1024 || slot < 0 || slot >= a.num_slots || S < 0 ||
              S * kB + (protect ? a.w : 0) > a.k;
   const int nt = (n + kB - 1) / kB;
   const int32_t* src_tab = a.src_table + static_cast<int64_t>(r) * a.max_blocks;
   const int32_t* dst_tab = a.dst_table + static_cast<int64_t>(r) * a.n_max;
   if (!bad) {
-    for (int j = tid; j < nt; j += kThreads)
-      bad |= src_tab[j] < 0 || src_tab[j] >= a.NB;
+    for (int j = tid; j < nt; j += kThreads) {
+      const int b = src_tab[j];
+      bad |= b < 0 || b >= a.NB;
+      tab[j] = b;
+    }
     for (int j = tid; j < a.n_max; j += kThreads)
       bad |= dst_tab[j] < 0 || dst_tab[j] >= a.NB;
   }
@@ -102,26 +173,21 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(ScoreArgs a) {
     return;
   }
 
-  const int64_t tile_elems = static_cast<int64_t>(kB) * D;
   const char* kbase = static_cast<const char*>(a.kpool) +
-                      (static_cast<int64_t>(l) * a.NB * a.Hkv + h) * tile_elems *
-                          E::kBytes;
-  const int64_t block_stride = static_cast<int64_t>(a.Hkv) * tile_elems * E::kBytes;
-  const int lane_off = (nl * D + jg * (D / 4)) * E::kBytes;
+                      (static_cast<int64_t>(l) * a.NB * a.Hkv + h) * TG::kTileBytes;
+  const int64_t block_stride = static_cast<int64_t>(a.Hkv) * TG::kTileBytes;
 
-  // ---- the window rows of this unit as MFMA A fragments
-  FragT q[RT];
+  // ---- this wave's window rows as MFMA A fragments
+  FragT q[RTW];
   {
     const char* qbase = static_cast<const char*>(a.q_window) +
-                        static_cast<int64_t>(slot * a.L + l) * a.w * a.Hq * D *
-                            E::kBytes;
+                        static_cast<int64_t>(slot * a.L + l) * a.w * a.Hq * D * E::kBytes;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const int row = rt * 16 + nl;
-      if (row < a.wG) {
+    for (int rt = 0; rt < RTW; ++rt) {
+      const int row = (rt0 + rt) * 16 + nl;
+      if (rt < nrt && row < a.wG) {
         const int i = row / a.G, g = row - i * a.G;
-        q[rt].load(qbase + (static_cast<int64_t>(i) * a.Hq + h * a.G + g) * D *
-                               E::kBytes +
+        q[rt].load(qbase + (static_cast<int64_t>(i) * a.Hq + h * a.G + g) * D * E::kBytes +
                    jg * (D / 4) * E::kBytes);
       } else {
         q[rt].zero();
@@ -130,171 +196,297 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(ScoreArgs a) {
   }
   for (int row = tid; row < kRows; row += kThreads)
     rowpos[row] = row < a.wG ? n - a.w + row / a.G : -1;
-  __syncthreads();
 
   const float sl2 = a.sl2;
+  const int nsteps = (nt + kQuarters - 1) / kQuarters;
+  auto tile_of = [&](int s) { return s * kQuarters + kq; };
   auto tile_masked = [&](int kt) {
     return (kt + 1) * kB > n || (causal && kt * kB + kB - 1 > n - a.w);
   };
-  auto load_tile = [&](FragT& f, int kt) {
-    if (kt < nt) {
-      const int blk = __builtin_amdgcn_readfirstlane(src_tab[kt]);
-      if (kt * kB + nl < n)
-        f.load(kbase + blk * block_stride + lane_off);
-      else
-        f.zero();
-    }
+  auto entry_ok = [&](int rt, int i, int t) {
+    const int p = rowpos[(rt0 + rt) * 16 + jg * 4 + i];
+    return t < n && (causal ? t <= p : p >= 0);
   };
+  // direct global->LDS loads of this wave's half of the block of step s.
+  // Lane offsets inside a block are fixed: the destination of load e is the
+  // 16-byte slot inst*64 + lane, which holds chunk (row, pos ^ swz(row)).
+  int src_off[TG::kLoadsPerWave];
+#pragma unroll
+  for (int e = 0; e < TG::kLoadsPerWave; ++e) {
+    const int sidx = (rg * TG::kLoadsPerWave + e) * 64 + lane;
+    const int row = sidx / TG::kRowChunks, pos = sidx % TG::kRowChunks;
+    src_off[e] = row * TG::kRowBytes + ((pos ^ (row & TG::kSwz)) << 4);
+  }
+  int frag_off[FragT::kChunks];
+#pragma unroll
+  for (int c = 0; c < FragT::kChunks; ++c)
+    frag_off[c] = TG::chunk_off(nl, jg * FragT::kChunks + c);
+  // last step that has a block for this quarter (-1: none)
+  const int last = kq < nt ? (nt - 1 - kq) / kQuarters : -1;
+  auto issue = [&](int s, int slot_w) {
+    const char* src = kbase + tab[tile_of(s)] * block_stride;
+    char* dst = ring[kq][slot_w] + rg * TG::kLoadsPerWave * 1024;
+#pragma unroll
+    for (int e = 0; e < TG::kLoadsPerWave; ++e)
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + src_off[e]),
+                                       (ZP_LDS void*)(dst + e * 1024), 16, 0, 0);
+  };
+  // this wave's loads of step s have landed once at most `ahead` later
+  // steps' loads are outstanding; then meet the other waves
+  auto arrive = [&](int s) {
+    const int ahead = min(kRing - 2, last - s);
+    if (ahead >= kRing - 2) {
+      wait_vm_lgkm0((kRing - 2) * TG::kLoadsPerWave);
+    } else {
+#pragma unroll
+      for (int d = kRing - 3; d >= 0; --d)
+        if (ahead == d) wait_vm_lgkm0(d * TG::kLoadsPerWave);
+      if (ahead < 0) wait_vm_lgkm0(0);
+    }
+    step_barrier();
+  };
+  auto read_frag = [&](FragT& f, int slot_r) {
+    const char* base = ring[kq][slot_r];
+#pragma unroll
+    for (int c = 0; c < FragT::kChunks; ++c)
+      f.v[c] = *reinterpret_cast<const zpd::u32x4_t*>(base + frag_off[c]);
+  };
+  // one sweep: body(frag, kt, s) for this quarter's blocks, kRing-1 ahead
+  auto sweep = [&](auto&& body) {
+    int slot_w = 0;
+    for (int p = 0; p < kRing - 1; ++p) {
+      if (p <= last) issue(p, slot_w);
+      slot_w = slot_w + 1 == kRing ? 0 : slot_w + 1;
+    }
+    int slot_r = 0;
+    for (int s = 0; s < nsteps; ++s) {
+      arrive(s);
+      if (s + kRing - 1 <= last) issue(s + kRing - 1, slot_w);  // slot freed by step s-1
+      slot_w = slot_w + 1 == kRing ? 0 : slot_w + 1;
+      if (s <= last) {
+        FragT kc;
+        read_frag(kc, slot_r);
+        body(kc, tile_of(s), s);
+      }
+      slot_r = slot_r + 1 == kRing ? 0 : slot_r + 1;
+    }
+    wait_vm_lgkm0(0);
+    step_barrier();
+  };
+  __syncthreads();
 
   // ---- phase 1: row statistics and lightning redundancy
-  float m[RT][4], z[RT][4];
+  // Each wave takes a per-row reference r (exp2 domain) from the maximum of
+  // its first key block and accumulates z = sum exp2(x*sl2 - r) with no
+  // running maximum. fp32 absorbs any later growth below 2^127; a row whose
+  // sum overflows (or that saw no valid key first) sends the unit through
+  // the exact online pass below.
+  float mr[RTW][4], z[RTW][4];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
+  for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      m[rt][i] = -INFINITY;
       z[rt][i] = 0.f;
+      mr[rt][i] = -INFINITY;
     }
-  {
-    FragT kc, kn;
-    load_tile(kc, wave);
-    for (int kt = wave; kt < nt; kt += kWaves) {
-      load_tile(kn, kt + kWaves);
-      f32x4_t acc[RT];
+  sweep([&](const FragT& kc, int kt, int s) {
+    const int t = kt * kB + nl;
+    f32x4_t acc[RTW];
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-        acc[rt] = zpd::mma_rows<E, D>(q[rt], kc, f32x4_t{0.f, 0.f, 0.f, 0.f});
-      const f32x4_t gram =
-          zpd::mma_rows<E, D>(kc, kc, f32x4_t{0.f, 0.f, 0.f, 0.f});
-      const int t = kt * kB + nl;
-      if (!tile_masked(kt)) {
+    for (int rt = 0; rt < RTW; ++rt)
+      acc[rt] = rt < nrt ? zpd::mma_rows<E, D>(q[rt], kc, f32x4_t{0.f, 0.f, 0.f, 0.f})
+                         : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (s == 0) {  // first block of this wave: the references
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float x = acc[rt][i];
-            const float dl = x - m[rt][i];
-            const float e = zpd::fast_exp2(-fabsf(dl) * sl2);
-            const bool up = dl > 0.f;
-            z[rt][i] = up ? fmaf(z[rt][i], e, 1.f) : z[rt][i] + e;
-            m[rt][i] = up ? x : m[rt][i];
-          }
-      } else {
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int p = rowpos[rt * 16 + jg * 4 + i];
-            const bool ok = t < n && (causal ? t <= p : p >= 0);
-            if (ok) {
-              const float x = acc[rt][i];
-              const float dl = x - m[rt][i];
-              const float e = zpd::fast_exp2(-fabsf(dl) * sl2);
-              const bool up = dl > 0.f;
-              z[rt][i] = up ? fmaf(z[rt][i], e, 1.f) : z[rt][i] + e;
-              m[rt][i] = up ? x : m[rt][i];
-            }
-          }
-      }
-      // lightning redundancy of block kt: column sums of the cosine matrix
-      {
-        float sq = kc.sumsq();
-        sq += zpd::shfl_xor(sq, 16);
-        sq += zpd::shfl_xor(sq, 32);
-        const float nrm = sqrtf(sq);  // norm of key nl (every j holds it)
-        const int cnt = min(kB, n - kt * kB);
-        float cs = 0.f;
+      for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int rw = jg * 4 + i;
-          const float nr = __shfl(nrm, rw, 64);
-          if (rw != nl && rw < cnt && nl < cnt)
-            cs += gram[i] / fmaxf(nr * nrm, 1e-8f);
-        }
-        cs += zpd::shfl_xor(cs, 16);
-        cs += zpd::shfl_xor(cs, 32);
-        if (jg == 0 && nl < cnt) s_tok[t] = cnt >= 2 ? cs / (cnt - 1) : 0.f;
-      }
-      kc = kn;
-    }
-  }
-  // reduce statistics over the 16 lanes that share rows, then over waves
+          float v = entry_ok(rt, i, t) ? acc[rt][i] * sl2 : -INFINITY;
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
+          for (int o = 1; o < 16; o <<= 1) v = fmaxf(v, zpd::shfl_xor(v, o));
+          mr[rt][i] = v;
+        }
+    }
+    if (!tile_masked(kt)) {
+#pragma unroll
+      for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          z[rt][i] += zpd::fast_exp2(fmaf(acc[rt][i], sl2, -mr[rt][i]));
+    } else {
+#pragma unroll
+      for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (entry_ok(rt, i, t))
+            z[rt][i] += zpd::fast_exp2(fmaf(acc[rt][i], sl2, -mr[rt][i]));
+    }
+    // lightning redundancy of block kt (the pair alternates by step):
+    // column sums of the block's cosine matrix
+    if ((s & 1) == rg) {
+      // squared norms sit on the Gram diagonal: column nl's is element
+      // nl & 3 of lane (nl >> 2, nl); cos = g * rsqrt(max(|a|^2 |b|^2, 1e-16))
+      const f32x4_t gram = zpd::mma_rows<E, D>(kc, kc, f32x4_t{0.f, 0.f, 0.f, 0.f});
+      const int di = nl & 3;
+      const float own = di == 0 ? gram[0] : di == 1 ? gram[1] : di == 2 ? gram[2] : gram[3];
+      const float dg = __shfl(own, (nl >> 2) * 16 + nl, 64);   // |k_nl|^2
+      const int cnt = min(kB, n - kt * kB);
+      float cs = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rw = jg * 4 + i;
+        const float dr = __shfl(dg, rw, 64);                     // |k_rw|^2
+        if (rw != nl && rw < cnt && nl < cnt)
+          cs += gram[i] * __builtin_amdgcn_rsqf(fmaxf(dr * dg, 1e-16f));
+      }
+      cs += zpd::shfl_xor(cs, 16);
+      cs += zpd::shfl_xor(cs, 32);
+      if (jg == 0 && nl < cnt) s_tok[t] = cnt >= 2 ? cs / (cnt - 1) : 0.f;
+    }
+  });
+  // the 16 lanes sharing rows share the reference: their sums just add up
+#pragma unroll
+  for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        const float m2 = zpd::shfl_xor(m[rt][i], o);
-        const float z2 = zpd::shfl_xor(z[rt][i], o);
-        zpd::merge_stats(m[rt][i], z[rt][i], m2, z2, sl2);
-      }
-      if (nl == 0) {
-        st_m[wave][rt * 16 + jg * 4 + i] = m[rt][i];
-        st_z[wave][rt * 16 + jg * 4 + i] = z[rt][i];
+      for (int o = 1; o < 16; o <<= 1) z[rt][i] += zpd::shfl_xor(z[rt][i], o);
+      if (nl == 0 && rt < nrt) {
+        st_m[kq][(rt0 + rt) * 16 + jg * 4 + i] = mr[rt][i];
+        st_z[kq][(rt0 + rt) * 16 + jg * 4 + i] = z[rt][i];
       }
     }
   __syncthreads();
+  bool redo = false;
   for (int row = tid; row < kRows; row += kThreads) {
     float mm = st_m[0][row], zz = st_z[0][row];
-    for (int v = 1; v < kWaves; ++v) zpd::merge_stats(mm, zz, st_m[v][row], st_z[v][row], sl2);
+    for (int v = 1; v < kQuarters; ++v) zpd::merge_stats(mm, zz, st_m[v][row], st_z[v][row], 1.f);
+    if (row < a.wG && !(zz > 0.f && zz < INFINITY && mm > -INFINITY)) redo = true;
     // p = exp2(x*sl2 - mprime) is the normalised probability of a row entry
-    mprime[row] = (row < a.wG && zz > 0.f) ? mm * sl2 + __log2f(zz) : INFINITY;
+    mprime[row] = (row < a.wG) ? mm + __log2f(zz) : INFINITY;
+  }
+  if (__syncthreads_or(redo)) {
+    // exact pass: per-lane online maximum and sum (keys read once more)
+    float m[RTW][4];
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        m[rt][i] = -INFINITY;
+        z[rt][i] = 0.f;
+      }
+    sweep([&](const FragT& kc, int kt, int) {
+      const int t = kt * kB + nl;
+      const bool masked = tile_masked(kt);
+#pragma unroll
+      for (int rt = 0; rt < RTW; ++rt) {
+        if (rt >= nrt) continue;
+        const f32x4_t acc = zpd::mma_rows<E, D>(q[rt], kc, f32x4_t{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (masked && !entry_ok(rt, i, t)) continue;
+          const float x = acc[i] * sl2;
+          const float dl = x - m[rt][i];
+          const float e = zpd::fast_exp2(-fabsf(dl));
+          const bool up = dl > 0.f;
+          z[rt][i] = up ? fmaf(z[rt][i], e, 1.f) : z[rt][i] + e;
+          m[rt][i] = up ? x : m[rt][i];
+        }
+      }
+    });
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+          const float m2 = zpd::shfl_xor(m[rt][i], o);
+          const float z2 = zpd::shfl_xor(z[rt][i], o);
+          zpd::merge_stats(m[rt][i], z[rt][i], m2, z2, 1.f);
+        }
+        if (nl == 0 && rt < nrt) {
+          st_m[kq][(rt0 + rt) * 16 + jg * 4 + i] = m[rt][i];
+          st_z[kq][(rt0 + rt) * 16 + jg * 4 + i] = z[rt][i];
+        }
+      }
+    __syncthreads();
+    for (int row = tid; row < kRows; row += kThreads) {
+      float mm = st_m[0][row], zz = st_z[0][row];
+      for (int v = 1; v < kQuarters; ++v) zpd::merge_stats(mm, zz, st_m[v][row], st_z[v][row], 1.f);
+      mprime[row] = (row < a.wG && zz > 0.f) ? mm + __log2f(zz) : INFINITY;
+    }
   }
   __syncthreads();
 
   // ---- phase 2: column means, score combination
-  float mp[RT][4];
+  // Each wave sums its half of the rows; the second half's partial column
+  // sums reach the first half through LDS one step later, where the token's
+  // attention and score are completed.
+  float mp[RTW][4];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
+  for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) mp[rt][i] = mprime[rt * 16 + jg * 4 + i];
+    for (int i = 0; i < 4; ++i)
+      mp[rt][i] = rt < nrt ? mprime[(rt0 + rt) * 16 + jg * 4 + i] : INFINITY;
   const float inv_rows = 1.f / static_cast<float>(a.wG);
   const int64_t urow = static_cast<int64_t>(u) * a.n_cap;
   const float* grow = a.glob + (static_cast<int64_t>(slot * a.L + l) * a.Hkv + h) * a.n_cap;
   const int pin_lo = S * kB;
   const int pin_hi = protect ? n - a.w : n;
-  {
-    FragT kc, kn;
-    load_tile(kc, wave);
-    for (int kt = wave; kt < nt; kt += kWaves) {
-      load_tile(kn, kt + kWaves);
-      f32x4_t acc[RT];
+  float cs_prev = 0.f;
+  // Inside the sweep only stores are issued (a load whose value is needed
+  // would have to wait for every key load issued before it): the attention
+  // of a block goes straight to the output row, and scores are formed after
+  // the sweep.
+  auto finish = [&](int kt, float cs) {  // rg == 0, lanes jg == 0
+    const int t = kt * kB + nl;
+    if (t < n) a.attn[urow + t] = cs * inv_rows;
+  };
+  sweep([&](const FragT& kc, int kt, int s) {
+    if (rg == 0 && s > 0 && jg == 0)  // the previous block of this quarter
+      finish(tile_of(s - 1), cs_prev + xchg[kq][(s - 1) & 1][nl]);
+    const int t = kt * kB + nl;
+    float cs = 0.f;
+    if (!tile_masked(kt)) {
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-        acc[rt] = zpd::mma_rows<E, D>(q[rt], kc, f32x4_t{0.f, 0.f, 0.f, 0.f});
-      const int t = kt * kB + nl;
-      float cs = 0.f;
-      if (!tile_masked(kt)) {
+      for (int rt = 0; rt < RTW; ++rt)
+        if (rt < nrt) {
+          const f32x4_t acc = zpd::mma_rows<E, D>(q[rt], kc, f32x4_t{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
+          for (int i = 0; i < 4; ++i) cs += zpd::fast_exp2(fmaf(acc[i], sl2, -mp[rt][i]));
+        }
+    } else {
+#pragma unroll
+      for (int rt = 0; rt < RTW; ++rt)
+        if (rt < nrt) {
+          const f32x4_t acc = zpd::mma_rows<E, D>(q[rt], kc, f32x4_t{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            cs += zpd::fast_exp2(fmaf(acc[rt][i], sl2, -mp[rt][i]));
-      } else {
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int p = rowpos[rt * 16 + jg * 4 + i];
-            const bool ok = t < n && (causal ? t <= p : p >= 0);
-            if (ok) cs += zpd::fast_exp2(fmaf(acc[rt][i], sl2, -mp[rt][i]));
-          }
-      }
-      cs += zpd::shfl_xor(cs, 16);
-      cs += zpd::shfl_xor(cs, 32);
-      if (jg == 0 && t < n) {
-        const float at = cs * inv_rows;
-        const float rd = s_tok[t];
-        float s = fmaf(a.w_attn, at, fmaf(a.w_global, grow[t], -a.w_red * rd));
-        if (t < pin_lo || t >= pin_hi) s = INFINITY;
-        a.attn[urow + t] = at;
-        if (a.red) a.red[urow + t] = rd;
-        if (a.score) a.score[urow + t] = s;
-        s_tok[t] = __uint_as_float(zpd::order_key(s));
-      }
-      kc = kn;
+            if (entry_ok(rt, i, t)) cs += zpd::fast_exp2(fmaf(acc[i], sl2, -mp[rt][i]));
+        }
     }
+    cs += zpd::shfl_xor(cs, 16);
+    cs += zpd::shfl_xor(cs, 32);
+    if (rg == 1) {
+      if (jg == 0) xchg[kq][s & 1][nl] = cs;
+    } else {
+      cs_prev = cs;
+    }
+  });
+  // the sweep ended with a barrier: finish each quarter's last block
+  if (rg == 0 && jg == 0 && kq < nt) {
+    const int s_last = (nt - 1 - kq) / kQuarters;  // last step with a block here
+    finish(tile_of(s_last), cs_prev + xchg[kq][s_last & 1][nl]);
+  }
+  __syncthreads();  // the attention row is complete (same workgroup, via L2)
+  for (int t = tid; t < n; t += kThreads) {
+    const float at = a.attn[urow + t];
+    const float rd = s_tok[t];
+    float sc = fmaf(a.w_attn, at, fmaf(a.w_global, grow[t], -a.w_red * rd));
+    if (t < pin_lo || t >= pin_hi) sc = INFINITY;
+    if (a.red) a.red[urow + t] = rd;
+    if (a.score) a.score[urow + t] = sc;
+    s_tok[t] = __uint_as_float(zpd::order_key(sc));
   }
   __syncthreads();
 
@@ -305,17 +497,23 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(ScoreArgs a) {
   int want = E_total;  // rank (1-based) of the threshold among the remaining
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
-    hist[tid] = 0;
+    for (int i = tid; i < kWaves * 257; i += kThreads) (&hist[0][0])[i] = 0;
     __syncthreads();
     for (int t = tid; t < n; t += kThreads) {
       const uint32_t key = keys[t];
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      if ((key & pmask) == prefix) atomicAdd(&hist[wave][(key >> shift) & 255u], 1u);
     }
     __syncthreads();
     if (wave == 0) {
-      // inclusive scan of 256 bins, 4 per lane
-      const uint32_t h0 = hist[lane * 4], h1 = hist[lane * 4 + 1],
-                     h2 = hist[lane * 4 + 2], h3 = hist[lane * 4 + 3];
+      // inclusive scan of 256 bins (summed over the waves), 4 per lane
+      uint32_t h0 = 0, h1 = 0, h2 = 0, h3 = 0;
+#pragma unroll
+      for (int w2 = 0; w2 < kWaves; ++w2) {
+        h0 += hist[w2][lane * 4];
+        h1 += hist[w2][lane * 4 + 1];
+        h2 += hist[w2][lane * 4 + 2];
+        h3 += hist[w2][lane * 4 + 3];
+      }
       const uint32_t loc = h0 + h1 + h2 + h3;
       uint32_t x = loc;
 #pragma unroll
@@ -352,7 +550,7 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(ScoreArgs a) {
   int my_ties = 0;
   for (int t = t0; t < t1; ++t) my_ties += keys[t] == thr;
   int ties_total;
-  const int ties_before = zpd::block_exclusive_scan(my_ties, scratch, &ties_total);
+  const int ties_before = zpd::block_exclusive_scan<kWaves>(my_ties, scratch, &ties_total);
   const int ties_after = ties_total - ties_before - my_ties;
   uint64_t evict = 0;
   int seen = 0, kept = 0, first_ev = n;
@@ -372,14 +570,14 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(ScoreArgs a) {
     }
   }
   int kept_total;
-  const int off = zpd::block_exclusive_scan(kept, scratch, &kept_total);
+  const int off = zpd::block_exclusive_scan<kWaves>(kept, scratch, &kept_total);
   int32_t* keep_row = a.keep + static_cast<int64_t>(u) * a.k;
   if (kept_total == a.k) {
     int o = off;
     for (int t = t0; t < t1; ++t)
       if (!((evict >> (t - t0)) & 1ull)) keep_row[o++] = t;
   }
-  const int hole = zpd::block_min(first_ev, scratch);
+  const int hole = zpd::block_min<kWaves>(first_ev, scratch);
   if (tid == 0) {
     if (kept_total != a.k) {  // cannot happen for a consistent unit
       a.hole[u] = -1;
@@ -396,25 +594,31 @@ zp_status launch_one(const zp::CompressGeom& g, const ScoreArgs& args,
                      void* stream) {
   const size_t dyn = static_cast<size_t>(g.n_cap) * sizeof(float);
   auto kern = score_select_kernel<E, D, RT>;
-  if (dyn > 48 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(dyn));
-    if (e != hipSuccess)
-      return zp::fail(ZP_EHIP, "score kernel attribute: %s", hipGetErrorString(e));
-  }
+  hipFuncAttributes fa;
+  hipError_t e = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(kern));
+  if (e != hipSuccess)
+    return zp::fail(ZP_EHIP, "score kernel attributes: %s", hipGetErrorString(e));
+  if (fa.sharedSizeBytes + dyn > 160 * 1024)
+    return zp::fail(ZP_EUNSUPPORTED, "n_cap %d: %zu bytes of token scores do not fit "
+                    "beside %zu bytes of key ring in LDS", g.n_cap, dyn,
+                    static_cast<size_t>(fa.sharedSizeBytes));
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     static_cast<int>(dyn));
+  if (e != hipSuccess)
+    return zp::fail(ZP_EHIP, "score kernel attribute: %s", hipGetErrorString(e));
   const unsigned units = static_cast<unsigned>(g.R) * g.L * g.Hkv;
   hipLaunchKernelGGL(kern, dim3(units), dim3(kThreads), dyn,
                      static_cast<hipStream_t>(stream), args);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess)
     return zp::fail(ZP_EHIP, "score kernel launch: %s", hipGetErrorString(e));
   return ZP_OK;
 }
 
-// Window rows are padded to 16, 32, 64, 128 or 192; the query fragments of
-// all rows stay in registers, so fp32 with head_dim 128 stops at 64 rows
-// (beyond that the fragments would spill).
+// Window rows are padded to 16, 32, 64, 128 or 192 and split between the
+// two row halves; each half keeps its query fragments in registers.
+// (fp32 with head_dim 128 stops at 64 rows: beyond that the fragments spill).
 template <typename E, int D>
 zp_status dispatch_rows(const zp::CompressGeom& g, const ScoreArgs& args,
                         void* stream) {

@@ -125,9 +125,10 @@ __device__ __forceinline__ void merge_stats(float& m, float& z, float m2,
   z = a + b;
 }
 
-// Block-wide exclusive prefix sum over 256 threads (4 waves); returns the
-// exclusive prefix of `v` and stores the total in *total. `scratch` holds at
-// least 4 ints of LDS. Contains __syncthreads; every thread must call it.
+// Block-wide exclusive prefix sum over W waves; returns the exclusive
+// prefix of `v` and stores the total in *total. `scratch` holds at least W
+// ints of LDS. Contains __syncthreads; every thread must call it.
+template <int W>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch,
                                                     int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -141,7 +142,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch,
   __syncthreads();
   int before = 0, all = 0;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < W; ++w) {
     const int t = scratch[w];
     if (w < wave) before += t;
     all += t;
@@ -151,6 +152,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch,
   return before + x - v;
 }
 
+template <int W>
 __device__ __forceinline__ int block_min(int v, int* scratch) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -159,7 +161,7 @@ __device__ __forceinline__ int block_min(int v, int* scratch) {
   __syncthreads();
   int r = scratch[0];
 #pragma unroll
-  for (int w = 1; w < 4; ++w) r = min(r, scratch[w]);
+  for (int w = 1; w < W; ++w) r = min(r, scratch[w]);
   __syncthreads();
   return r;
 }

@@ -47,6 +47,7 @@ class Case:
     global_override: Optional[np.ndarray] = None  # [R][L][Hkv][n_cap] or None
     identical_keys: bool = False
     use_block_manager: bool = False               # prefix plans from zp_bm
+    outlier: Optional[Tuple[int, float]] = None   # (logical position, scale)
 
 
 @dataclass
@@ -101,6 +102,12 @@ def build_inputs(case: Case, device: str = "cuda"):
             nxt += 1
     if case.identical_keys:
         wl.k_pool[:] = wl.k_pool[0, 0, 0, 0].clone()
+    if case.outlier is not None:
+        # one key per unit scaled up: its logits dwarf everything before it
+        pos, scale = case.outlier
+        for r in range(R):
+            blk = int(tables[r, pos // b])
+            wl.k_pool[:, blk, :, pos % b, :] *= scale
     glob = wl.global_scores
     if n_cap != wl.n_cap:
         g2 = torch.rand((glob.shape[0], glob.shape[1], glob.shape[2], n_cap),

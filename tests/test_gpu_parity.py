@@ -110,6 +110,14 @@ def test_adversarial_keep_sets(name, positions):
     _check(P.Case(spec, global_override=_forced_global(spec, positions)), name)
 
 
+def test_outlier_key_takes_the_exact_softmax_pass():
+    # logits of the scaled key exceed the first block's reference by far more
+    # than 128 in the exp2 domain: the reference sums overflow and the unit is
+    # re-scored with the exact online pass
+    spec = synth.scaled(EIGHT_B, requests=2)
+    _check(P.Case(spec, outlier=(100, 100.0)), "outlier key x100 at t=100")
+
+
 def test_forced_ties_keep_prefix():
     spec = synth.scaled(EIGHT_B, requests=1, layers=1)
     g = np.full((1, 1, spec.kv_heads, spec.n_tokens), 0.25)
