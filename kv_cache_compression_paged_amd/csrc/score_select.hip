@@ -102,10 +102,13 @@ struct TileGeom {
   static constexpr int kLoads = kTileBytes / 1024;          // per block
   static constexpr int kLoadsPerWave = kLoads / 2;          // per wave of a pair
   static constexpr int kSwz = kRowChunks < 16 ? kRowChunks - 1 : 15;
-  static constexpr int kRing0 = 96 * 1024 / (kQuarters * kTileBytes);
-  static constexpr int kRing = kRing0 > 8 ? 8 : kRing0;     // slots per quarter
+#ifndef ZP_RING_KIB
+#define ZP_RING_KIB 112
+#endif
+  static constexpr int kRing0 = ZP_RING_KIB * 1024 / (kQuarters * kTileBytes);
+  static constexpr int kRing = kRing0 > 8 ? 8 : (kRing0 < 4 ? 4 : kRing0);  // slots per quarter
   static_assert(kLoadsPerWave >= 1, "tile too small");
-  static_assert(kRing >= 3, "ring too short");
+  static_assert(kRing >= 4, "ring too short");
   static_assert((kRing - 1) * kLoadsPerWave <= 28, "wait count range");
   // LDS byte offset of chunk (row, c) inside a slot
   __device__ static constexpr int chunk_off(int row, int c) {
@@ -127,13 +130,14 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(ScoreArgs a) {
   __shared__ float st_z[kQuarters][kRows];
   __shared__ float mprime[kRows];
   __shared__ int rowpos[kRows];
-  __shared__ float xchg[kQuarters][2][16];
+  __shared__ float xchg[kQuarters][4][16];
   __shared__ int scratch[16];
   __shared__ uint32_t hist[kWaves][257];  // one padded histogram per wave
   __shared__ int sel[2];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int kq = wave & 3, rg = wave >> 2;
   const int jg = lane >> 4, nl = lane & 15;
   const int u = blockIdx.x;
@@ -223,6 +227,10 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(ScoreArgs a) {
     frag_off[c] = TG::chunk_off(nl, jg * FragT::kChunks + c);
   // last step that has a block for this quarter (-1: none)
   const int last = kq < nt ? (nt - 1 - kq) / kQuarters : -1;
+  struct Acc {
+    f32x4_t a[RTW];
+    f32x4_t g;
+  };
   auto issue = [&](int s, int slot_w) {
     const char* src = kbase + tab[tile_of(s)] * block_stride;
     char* dst = ring[kq][slot_w] + rg * TG::kLoadsPerWave * 1024;
@@ -231,47 +239,79 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(ScoreArgs a) {
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + src_off[e]),
                                        (ZP_LDS void*)(dst + e * 1024), 16, 0, 0);
   };
-  // this wave's loads of step s have landed once at most `ahead` later
-  // steps' loads are outstanding; then meet the other waves
-  auto arrive = [&](int s) {
-    const int ahead = min(kRing - 2, last - s);
-    if (ahead >= kRing - 2) {
-      wait_vm_lgkm0((kRing - 2) * TG::kLoadsPerWave);
-    } else {
-#pragma unroll
-      for (int d = kRing - 3; d >= 0; --d)
-        if (ahead == d) wait_vm_lgkm0(d * TG::kLoadsPerWave);
-      if (ahead < 0) wait_vm_lgkm0(0);
-    }
-    step_barrier();
-  };
   auto read_frag = [&](FragT& f, int slot_r) {
     const char* base = ring[kq][slot_r];
 #pragma unroll
     for (int c = 0; c < FragT::kChunks; ++c)
       f.v[c] = *reinterpret_cast<const zpd::u32x4_t*>(base + frag_off[c]);
   };
-  // one sweep: body(frag, kt, s) for this quarter's blocks, kRing-1 ahead
-  auto sweep = [&](auto&& body) {
+  // One sweep over this quarter's blocks, two blocks (steps 2i and 2i+1)
+  // per barrier. Loads run ahead through a ring of kRing slots: the prologue
+  // issues steps 0..kRing-3 and iteration i refills the slots of steps 2i-2
+  // and 2i-1 with steps 2i+kRing-2 and 2i+kRing-1. At iteration i the wave
+  // waits until its own loads of steps <= 2i+1 have landed, meets the other
+  // waves (all of their halves landed, all of iteration i-1 done), then
+  // issues both blocks' MFMAs before their vector work. after(i) runs right
+  // after each barrier (and once more after the last iteration).
+  auto wait_land = [&](int target, int issued_max) {
+    const int ahead = min(issued_max, last) - target;  // later steps in flight
+    if (ahead >= kRing - 4) {
+      wait_vm_lgkm0((kRing - 4) * TG::kLoadsPerWave);
+    } else {
+#pragma unroll
+      for (int d = kRing - 5; d >= 1; --d)
+        if (ahead == d) wait_vm_lgkm0(d * TG::kLoadsPerWave);
+      if (ahead <= 0) wait_vm_lgkm0(0);
+    }
+    step_barrier();
+  };
+  auto sweep = [&](auto&& mma, auto&& valu, auto&& after) {
+    static_assert(kRing >= 4, "double steps need four ring slots");
     int slot_w = 0;
-    for (int p = 0; p < kRing - 1; ++p) {
+    for (int p = 0; p < kRing - 2; ++p) {
       if (p <= last) issue(p, slot_w);
       slot_w = slot_w + 1 == kRing ? 0 : slot_w + 1;
     }
     int slot_r = 0;
-    for (int s = 0; s < nsteps; ++s) {
-      arrive(s);
-      if (s + kRing - 1 <= last) issue(s + kRing - 1, slot_w);  // slot freed by step s-1
-      slot_w = slot_w + 1 == kRing ? 0 : slot_w + 1;
-      if (s <= last) {
+    const int niters = (nsteps + 1) / 2;
+    for (int i = 0; i < niters; ++i) {
+      const int sa = 2 * i, sb = 2 * i + 1;
+      wait_land(sb, sa + kRing - 3);
+      after(i);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        if (sa + kRing - 2 + e <= last) issue(sa + kRing - 2 + e, slot_w);
+        slot_w = slot_w + 1 == kRing ? 0 : slot_w + 1;
+      }
+      const int slot_b = slot_r + 1 == kRing ? 0 : slot_r + 1;
+      Acc acc_a, acc_b;
+      if (sa <= last) {
         FragT kc;
         read_frag(kc, slot_r);
-        body(kc, tile_of(s), s);
+        mma(kc, sa, acc_a);
       }
-      slot_r = slot_r + 1 == kRing ? 0 : slot_r + 1;
+      if (sb <= last) {
+        FragT kc;
+        read_frag(kc, slot_b);
+        mma(kc, sb, acc_b);
+      }
+      if (sa <= last) valu(acc_a, tile_of(sa), sa);
+      if (sb <= last) valu(acc_b, tile_of(sb), sb);
+      slot_r = slot_b + 1 == kRing ? 0 : slot_b + 1;
     }
     wait_vm_lgkm0(0);
     step_barrier();
+    after(niters);
+  };
+  auto no_after = [](int) {};
+  // logits of this wave's rows against one block (plus, when asked, the
+  // block's 16x16 key Gram matrix)
+  auto logits = [&](const FragT& kc, Acc& acc, bool gram) {
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt)
+      acc.a[rt] = rt < nrt ? zpd::mma_rows<E, D>(q[rt], kc, f32x4_t{0.f, 0.f, 0.f, 0.f})
+                           : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (gram) acc.g = zpd::mma_rows<E, D>(kc, kc, f32x4_t{0.f, 0.f, 0.f, 0.f});
   };
   __syncthreads();
 
@@ -289,19 +329,15 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(ScoreArgs a) {
       z[rt][i] = 0.f;
       mr[rt][i] = -INFINITY;
     }
-  sweep([&](const FragT& kc, int kt, int s) {
+  sweep([&](const FragT& kc, int s, Acc& acc) { logits(kc, acc, (s & 1) == rg); },
+        [&](const Acc& acc, int kt, int s) {
     const int t = kt * kB + nl;
-    f32x4_t acc[RTW];
-#pragma unroll
-    for (int rt = 0; rt < RTW; ++rt)
-      acc[rt] = rt < nrt ? zpd::mma_rows<E, D>(q[rt], kc, f32x4_t{0.f, 0.f, 0.f, 0.f})
-                         : f32x4_t{0.f, 0.f, 0.f, 0.f};
     if (s == 0) {  // first block of this wave: the references
 #pragma unroll
       for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float v = entry_ok(rt, i, t) ? acc[rt][i] * sl2 : -INFINITY;
+          float v = entry_ok(rt, i, t) ? acc.a[rt][i] * sl2 : -INFINITY;
 #pragma unroll
           for (int o = 1; o < 16; o <<= 1) v = fmaxf(v, zpd::shfl_xor(v, o));
           mr[rt][i] = v;
@@ -312,21 +348,21 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(ScoreArgs a) {
       for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          z[rt][i] += zpd::fast_exp2(fmaf(acc[rt][i], sl2, -mr[rt][i]));
+          z[rt][i] += zpd::fast_exp2(fmaf(acc.a[rt][i], sl2, -mr[rt][i]));
     } else {
 #pragma unroll
       for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           if (entry_ok(rt, i, t))
-            z[rt][i] += zpd::fast_exp2(fmaf(acc[rt][i], sl2, -mr[rt][i]));
+            z[rt][i] += zpd::fast_exp2(fmaf(acc.a[rt][i], sl2, -mr[rt][i]));
     }
     // lightning redundancy of block kt (the pair alternates by step):
     // column sums of the block's cosine matrix
     if ((s & 1) == rg) {
       // squared norms sit on the Gram diagonal: column nl's is element
       // nl & 3 of lane (nl >> 2, nl); cos = g * rsqrt(max(|a|^2 |b|^2, 1e-16))
-      const f32x4_t gram = zpd::mma_rows<E, D>(kc, kc, f32x4_t{0.f, 0.f, 0.f, 0.f});
+      const f32x4_t& gram = acc.g;
       const int di = nl & 3;
       const float own = di == 0 ? gram[0] : di == 1 ? gram[1] : di == 2 ? gram[2] : gram[3];
       const float dg = __shfl(own, (nl >> 2) * 16 + nl, 64);   // |k_nl|^2
@@ -339,11 +375,11 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(ScoreArgs a) {
         if (rw != nl && rw < cnt && nl < cnt)
           cs += gram[i] * __builtin_amdgcn_rsqf(fmaxf(dr * dg, 1e-16f));
       }
-      cs += zpd::shfl_xor(cs, 16);
-      cs += zpd::shfl_xor(cs, 32);
+      cs = zpd::pairsum16(cs);
+      cs = zpd::pairsum32(cs);
       if (jg == 0 && nl < cnt) s_tok[t] = cnt >= 2 ? cs / (cnt - 1) : 0.f;
     }
-  });
+  }, no_after);
   // the 16 lanes sharing rows share the reference: their sums just add up
 #pragma unroll
   for (int rt = 0; rt < RTW; ++rt)
@@ -375,17 +411,17 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(ScoreArgs a) {
         m[rt][i] = -INFINITY;
         z[rt][i] = 0.f;
       }
-    sweep([&](const FragT& kc, int kt, int) {
+    sweep([&](const FragT& kc, int, Acc& acc) { logits(kc, acc, false); },
+          [&](const Acc& acc, int kt, int) {
       const int t = kt * kB + nl;
       const bool masked = tile_masked(kt);
 #pragma unroll
       for (int rt = 0; rt < RTW; ++rt) {
         if (rt >= nrt) continue;
-        const f32x4_t acc = zpd::mma_rows<E, D>(q[rt], kc, f32x4_t{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           if (masked && !entry_ok(rt, i, t)) continue;
-          const float x = acc[i] * sl2;
+          const float x = acc.a[rt][i] * sl2;
           const float dl = x - m[rt][i];
           const float e = zpd::fast_exp2(-fabsf(dl));
           const bool up = dl > 0.f;
@@ -393,7 +429,7 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(ScoreArgs a) {
           m[rt][i] = up ? x : m[rt][i];
         }
       }
-    });
+    }, no_after);
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
@@ -433,51 +469,48 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(ScoreArgs a) {
   const float* grow = a.glob + (static_cast<int64_t>(slot * a.L + l) * a.Hkv + h) * a.n_cap;
   const int pin_lo = S * kB;
   const int pin_hi = protect ? n - a.w : n;
-  float cs_prev = 0.f;
+  float cs_prev[2] = {0.f, 0.f};
   // Inside the sweep only stores are issued (a load whose value is needed
   // would have to wait for every key load issued before it): the attention
   // of a block goes straight to the output row, and scores are formed after
-  // the sweep.
-  auto finish = [&](int kt, float cs) {  // rg == 0, lanes jg == 0
-    const int t = kt * kB + nl;
-    if (t < n) a.attn[urow + t] = cs * inv_rows;
+  // the sweep. The second row half hands its partial column sums over through
+  // xchg (one buffer per step mod 4); the first half completes them one
+  // iteration later, after the barrier that orders the two.
+  auto finish = [&](int s, float cs) {  // rg == 0, lanes jg == 0
+    const int t = tile_of(s) * kB + nl;
+    if (t < n) a.attn[urow + t] = (cs + xchg[kq][s & 3][nl]) * inv_rows;
   };
-  sweep([&](const FragT& kc, int kt, int s) {
-    if (rg == 0 && s > 0 && jg == 0)  // the previous block of this quarter
-      finish(tile_of(s - 1), cs_prev + xchg[kq][(s - 1) & 1][nl]);
+  sweep([&](const FragT& kc, int, Acc& acc) { logits(kc, acc, false); },
+        [&](const Acc& acc, int kt, int s) {
     const int t = kt * kB + nl;
     float cs = 0.f;
     if (!tile_masked(kt)) {
 #pragma unroll
       for (int rt = 0; rt < RTW; ++rt)
-        if (rt < nrt) {
-          const f32x4_t acc = zpd::mma_rows<E, D>(q[rt], kc, f32x4_t{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-          for (int i = 0; i < 4; ++i) cs += zpd::fast_exp2(fmaf(acc[i], sl2, -mp[rt][i]));
-        }
+        for (int i = 0; i < 4; ++i) cs += zpd::fast_exp2(fmaf(acc.a[rt][i], sl2, -mp[rt][i]));
     } else {
 #pragma unroll
       for (int rt = 0; rt < RTW; ++rt)
-        if (rt < nrt) {
-          const f32x4_t acc = zpd::mma_rows<E, D>(q[rt], kc, f32x4_t{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (entry_ok(rt, i, t)) cs += zpd::fast_exp2(fmaf(acc[i], sl2, -mp[rt][i]));
-        }
+        for (int i = 0; i < 4; ++i)
+          if (entry_ok(rt, i, t)) cs += zpd::fast_exp2(fmaf(acc.a[rt][i], sl2, -mp[rt][i]));
     }
-    cs += zpd::shfl_xor(cs, 16);
-    cs += zpd::shfl_xor(cs, 32);
+    cs = zpd::pairsum16(cs);
+    cs = zpd::pairsum32(cs);
     if (rg == 1) {
-      if (jg == 0) xchg[kq][s & 1][nl] = cs;
+      if (jg == 0) xchg[kq][s & 3][nl] = cs;
     } else {
-      cs_prev = cs;
+      cs_prev[s & 1] = cs;
+    }
+  }, [&](int i) {  // complete the blocks of iteration i-1
+    if (i == 0 || rg != 0 || jg != 0) return;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int s = 2 * (i - 1) + e;
+      if (s <= last) finish(s, cs_prev[e]);
     }
   });
-  // the sweep ended with a barrier: finish each quarter's last block
-  if (rg == 0 && jg == 0 && kq < nt) {
-    const int s_last = (nt - 1 - kq) / kQuarters;  // last step with a block here
-    finish(tile_of(s_last), cs_prev + xchg[kq][s_last & 1][nl]);
-  }
   __syncthreads();  // the attention row is complete (same workgroup, via L2)
   for (int t = tid; t < n; t += kThreads) {
     const float at = a.attn[urow + t];

@@ -115,6 +115,20 @@ __device__ __forceinline__ float shfl_xor(float v, int m) {
   return __shfl_xor(v, m, 64);
 }
 
+// v + v(lane ^ 16) and v + v(lane ^ 32) in every lane, on the VALU
+// (v_permlane16_swap / v_permlane32_swap exchange 16-lane rows / 32-lane
+// halves; with both operands equal, the two results hold the pair).
+__device__ __forceinline__ float pairsum16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pairsum32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Merge two partial softmax statistics (max m, sum z of exp2((x-m)*sl2)).
 __device__ __forceinline__ void merge_stats(float& m, float& z, float m2,
                                             float z2, float sl2) {
