@@ -164,7 +164,10 @@ zp_status zp_compress_workspace_bytes(const zp_kv_pool* pool,
  * here; see zp_update_global). workspace: device, 256-byte aligned, at least
  * zp_compress_workspace_bytes; it also receives the device error word.
  * Errors: ZP_EINVAL, ZP_EUNSUPPORTED (head_dim not 64/128, block_size not 16,
- * w*G > 256, n_cap > 16384), ZP_EWORKSPACE, ZP_EHIP. */
+ * w*G > 192 -- 64 for fp32 with head_dim 128 --, n_cap > 16384, or, for fp32
+ * with head_dim 128 only, n_cap above about 6700: the per-token scores of a
+ * unit live in on-chip memory beside the key ring), ZP_EWORKSPACE, ZP_EHIP.
+ * Nothing is written when an error is returned. */
 zp_status zp_compress(const zp_kv_pool* pool, const zp_batch* batch,
                       const void* q_window, const float* global_scores,
                       const zp_params* params, const zp_compress_out* out,

@@ -21,14 +21,16 @@
 // 4s + kq, each for its half of the window rows, whose MFMA A fragments
 // stay in registers for the whole unit. Key blocks reach LDS by direct
 // global->LDS loads (16 bytes per lane, 1 KiB fully coalesced per
-// instruction) into a ring of kRing slots per quarter, issued kRing-1 steps
-// ahead, so ~80 KiB per CU are in flight without costing registers; each
-// wave of the pair issues half of a block's loads. The 16-byte chunks of a
-// block row are XOR-swizzled by row in LDS, so the ds_read_b128 fragment
-// reads (lane (j, n) takes row n, chunk group j) hit distinct banks. A step
-// is fenced by an exact s_waitcnt on the wave's own loads plus a raw
-// s_barrier (a __syncthreads would drain every load in flight). Two waves
-// share a SIMD, so one's MFMA overlaps the other's exp/VALU work.
+// instruction) into a ring of NS slots per quarter (NS = 7 for bf16 with
+// head_dim 128, so up to five blocks per quarter are in flight without
+// costing registers); each wave of the pair issues half of a block's loads.
+// The 16-byte chunks of a block row are XOR-swizzled by row in LDS, so the
+// ds_read_b128 fragment reads (lane (j, n) takes row n, chunk group j) hit
+// distinct banks. Two steps share one fence: an exact s_waitcnt on the
+// wave's own loads plus a raw s_barrier (a __syncthreads would drain every
+// load in flight). Two waves share a SIMD, so one's MFMA overlaps the
+// other's exp/VALU work. Long contexts (token rows that do not fit beside
+// the default ring in LDS) take a 4-slot ring.
 #include <hip/hip_runtime.h>
 
 #include "zp_device.h"
@@ -67,6 +69,17 @@ struct ScoreArgs {
   float w_attn, w_global, w_red, sl2;  // sl2 = softmax scale * log2(e)
 };
 
+// Ring slots per quarter: about 112 KiB of LDS, 4 to 8 slots.
+#ifndef ZP_RING_KIB
+#define ZP_RING_KIB 112
+#endif
+template <typename E, int D>
+constexpr int default_slots() {
+  constexpr int n = ZP_RING_KIB * 1024 / (kQuarters * 16 * D * E::kBytes);
+  return n > 8 ? 8 : (n < 4 ? 4 : n);
+}
+constexpr int kLongSlots = 4;
+
 // s_waitcnt with vmcnt = n (0..28), expcnt untouched, lgkmcnt = 0.
 __device__ __forceinline__ void wait_vm_lgkm0(int n) {
 #define ZP_W(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (((N) >> 4) << 14) | (7 << 4))
@@ -94,7 +107,7 @@ __device__ __forceinline__ void step_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <typename E, int D>
+template <typename E, int D, int NS>
 struct TileGeom {
   static constexpr int kRowBytes = D * E::kBytes;          // 128, 256 or 512
   static constexpr int kRowChunks = kRowBytes / 16;         // 8, 16 or 32
@@ -102,13 +115,9 @@ struct TileGeom {
   static constexpr int kLoads = kTileBytes / 1024;          // per block
   static constexpr int kLoadsPerWave = kLoads / 2;          // per wave of a pair
   static constexpr int kSwz = kRowChunks < 16 ? kRowChunks - 1 : 15;
-#ifndef ZP_RING_KIB
-#define ZP_RING_KIB 112
-#endif
-  static constexpr int kRing0 = ZP_RING_KIB * 1024 / (kQuarters * kTileBytes);
-  static constexpr int kRing = kRing0 > 8 ? 8 : (kRing0 < 4 ? 4 : kRing0);  // slots per quarter
+  static constexpr int kRing = NS;  // slots per quarter
   static_assert(kLoadsPerWave >= 1, "tile too small");
-  static_assert(kRing >= 4, "ring too short");
+  static_assert(kRing >= 4 && kRing <= 8, "ring length");
   static_assert((kRing - 1) * kLoadsPerWave <= 28, "wait count range");
   // LDS byte offset of chunk (row, c) inside a slot
   __device__ static constexpr int chunk_off(int row, int c) {
@@ -116,24 +125,29 @@ struct TileGeom {
   }
 };
 
-template <typename E, int D, int RT>
+template <typename E, int D, int RT, int NS>
 __global__ __launch_bounds__(kThreads) void score_select_kernel(ScoreArgs a) {
   using FragT = Frag<E, D>;
-  using TG = TileGeom<E, D>;
+  using TG = TileGeom<E, D, NS>;
   constexpr int kRows = RT * 16;
   constexpr int RTW = (RT + 1) / 2;     // row tiles of the first row half
   constexpr int kRing = TG::kRing;
   __shared__ __attribute__((aligned(16))) char ring[kQuarters][kRing][TG::kTileBytes];
   extern __shared__ float s_tok[];  // [n_cap]: red, then order keys
   __shared__ int tab[1024];
-  __shared__ float st_m[kQuarters][kRows];
-  __shared__ float st_z[kQuarters][kRows];
   __shared__ float mprime[kRows];
   __shared__ int rowpos[kRows];
   __shared__ float xchg[kQuarters][4][16];
   __shared__ int scratch[16];
-  __shared__ uint32_t hist[kWaves][257];  // one padded histogram per wave
   __shared__ int sel[2];
+  // The ring is idle between sweeps (each ends with all loads landed and a
+  // barrier) and during the select: the per-quarter row statistics and the
+  // per-wave histograms live in it then.
+  static_assert(2 * kQuarters * kRows * 4 <= sizeof(ring) &&
+                kWaves * 257 * 4 <= sizeof(ring), "ring too small to alias");
+  float (*st_m)[kRows] = reinterpret_cast<float (*)[kRows]>(&ring[0][0][0]);
+  float (*st_z)[kRows] = reinterpret_cast<float (*)[kRows]>(&ring[0][0][0] + kQuarters * kRows * 4);
+  uint32_t (*hist)[257] = reinterpret_cast<uint32_t (*)[257]>(&ring[0][0][0]);  // one per wave
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -622,11 +636,11 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(ScoreArgs a) {
   }
 }
 
-template <typename E, int D, int RT>
+template <typename E, int D, int RT, int NS>
 zp_status launch_one(const zp::CompressGeom& g, const ScoreArgs& args,
                      void* stream) {
   const size_t dyn = static_cast<size_t>(g.n_cap) * sizeof(float);
-  auto kern = score_select_kernel<E, D, RT>;
+  auto kern = score_select_kernel<E, D, RT, NS>;
   hipFuncAttributes fa;
   hipError_t e = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(kern));
   if (e != hipSuccess)
@@ -649,6 +663,23 @@ zp_status launch_one(const zp::CompressGeom& g, const ScoreArgs& args,
   return ZP_OK;
 }
 
+// The default ring when the token rows fit beside it, else the 4-slot ring.
+template <typename E, int D, int RT>
+zp_status launch_ring(const zp::CompressGeom& g, const ScoreArgs& args,
+                      void* stream) {
+  constexpr int ns = default_slots<E, D>();
+  if constexpr (ns > kLongSlots) {
+    hipFuncAttributes fa;
+    const hipError_t e = hipFuncGetAttributes(
+        &fa, reinterpret_cast<const void*>(score_select_kernel<E, D, RT, ns>));
+    if (e != hipSuccess)
+      return zp::fail(ZP_EHIP, "score kernel attributes: %s", hipGetErrorString(e));
+    if (fa.sharedSizeBytes + static_cast<size_t>(g.n_cap) * sizeof(float) > 160 * 1024)
+      return launch_one<E, D, RT, kLongSlots>(g, args, stream);
+  }
+  return launch_one<E, D, RT, ns>(g, args, stream);
+}
+
 // Window rows are padded to 16, 32, 64, 128 or 192 and split between the
 // two row halves; each half keeps its query fragments in registers.
 // (fp32 with head_dim 128 stops at 64 rows: beyond that the fragments spill).
@@ -660,12 +691,12 @@ zp_status dispatch_rows(const zp::CompressGeom& g, const ScoreArgs& args,
   if (rt > kMaxRT)
     return zp::fail(ZP_EUNSUPPORTED, "window rows w*G = %d exceed %d for this "
                     "element type and head_dim", g.wG, kMaxRT * 16);
-  if (rt <= 1) return launch_one<E, D, 1>(g, args, stream);
-  if (rt <= 2) return launch_one<E, D, 2>(g, args, stream);
-  if (rt <= 4) return launch_one<E, D, 4>(g, args, stream);
+  if (rt <= 1) return launch_ring<E, D, 1>(g, args, stream);
+  if (rt <= 2) return launch_ring<E, D, 2>(g, args, stream);
+  if (rt <= 4) return launch_ring<E, D, 4>(g, args, stream);
   if constexpr (kMaxRT > 4) {
-    if (rt <= 8) return launch_one<E, D, 8>(g, args, stream);
-    return launch_one<E, D, 12>(g, args, stream);
+    if (rt <= 8) return launch_ring<E, D, 8>(g, args, stream);
+    return launch_ring<E, D, 12>(g, args, stream);
   }
   return zp::fail(ZP_EUNSUPPORTED, "window rows w*G = %d", g.wG);
 }

@@ -1,0 +1,157 @@
+"""GPU parity of the paged-decode consumer against the CPU oracle.
+
+Decode reads a request's cache through its block table ([zh] §2.3: after a
+compression the request decodes from its N_max-1 re-packed blocks plus the
+tail block). Outputs are fp32 softmax-weighted sums of V; the oracle is the
+float64 softmax(q.K^T/sqrt(d)) V on the same stored bits.
+
+Tolerance: every output element is a convex combination of V entries, so
+its fp32 rounding error is bounded by a few ulps of sum_t p_t |v_t|, a number
+of order max|v| ~ 4 for N(0, 1) values: |gpu - ref| <= 1e-4 |ref| + 1e-5.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import kv_cache_compression_paged_amd as Z
+from kv_cache_compression_paged_amd import synth
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+RTOL, ATOL = 1e-4, 1e-5
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _lengths(R, n, rng):
+    """Ragged lengths: single token, partial and exact blocks, full cache."""
+    fixed = [1, 15, 16, 17, n - 1, n]
+    out = [fixed[r] if r < len(fixed) else int(rng.integers(1, n + 1))
+           for r in range(R)]
+    return np.asarray(out, dtype=np.int32)
+
+
+def _decode_case(spec, label, seed):
+    _say(f"[decode] {label}: {spec}")
+    dev = "cuda"
+    wl = synth.make(spec, device=dev)
+    R, L = spec.requests, spec.layers
+    n = spec.n_tokens
+    rng = np.random.default_rng(seed)
+    lens = _lengths(R, n, rng)
+    q = synth.decode_queries(spec, R, dev, seed)
+    dt = Z.ZP_BF16 if spec.dtype == "bf16" else Z.ZP_F32
+    params = Z.make_params(spec.n_max, spec.window, spec.q_heads, dt)
+    pool = Z.make_pool(wl.k_pool, wl.v_pool)
+    out = torch.full((R, L, spec.q_heads, spec.head_dim), float("nan"),
+                     dtype=torch.float32, device=dev)
+    Z.zp_paged_decode(out, q, pool, torch.from_numpy(wl.tables).to(dev),
+                      torch.from_numpy(lens).to(dev), params)
+    torch.cuda.synchronize()
+    ref = O.paged_decode(synth.raw_numpy(q), spec.dtype, synth.raw_numpy(wl.k_pool),
+                         synth.raw_numpy(wl.v_pool), spec.dtype, wl.tables, lens)
+    got = out.cpu().numpy().astype(np.float64)
+    worst = 0.0
+    for (r, l), want in ref.items():
+        err = np.abs(got[r, l] - want)
+        bound = RTOL * np.abs(want) + ATOL
+        worst = max(worst, float(np.max(err / bound)))
+        assert np.all(err <= bound), (
+            f"request {r} (len {lens[r]}) layer {l}: max err {err.max():.3g}")
+    _say(f"[decode] {label}: ok, worst err/bound {worst:.3f}")
+
+
+DECODE_CASES = [
+    ("bf16 d128 G=4", synth.scaled(synth.EIGHT_B, requests=7, layers=2,
+                                   kv_heads=2, q_heads=8, n_max=20,
+                                   pool_blocks=7 * 20 + 3)),
+    ("bf16 d128 G=6", synth.scaled(synth.SMALL, requests=6, layers=2, n_max=9,
+                                   pool_blocks=6 * 9 + 2)),
+    ("bf16 d64 G=16", synth.scaled(synth.EIGHT_B, requests=6, layers=1,
+                                   kv_heads=1, q_heads=16, head_dim=64,
+                                   n_max=8, pool_blocks=6 * 8, near_dup=False)),
+    ("fp32 d64 G=2", synth.scaled(synth.TINY, requests=6, pool_blocks=6 * 8,
+                                  permute=True)),
+    ("fp32 d128 G=2", synth.scaled(synth.TINY, requests=6, kv_heads=1,
+                                   q_heads=2, head_dim=128, pool_blocks=6 * 8,
+                                   permute=True)),
+]
+
+
+@pytest.mark.parametrize("label,spec", DECODE_CASES, ids=[c[0] for c in DECODE_CASES])
+def test_decode_matches_oracle(label, spec):
+    _decode_case(spec, label, seed=77)
+
+
+def test_decode_after_compression():
+    """Compress, then decode the k kept tokens through the new tables: the
+    result equals the oracle's decode over the original rows of the kept
+    positions (compaction moved them byte for byte)."""
+    spec = synth.scaled(synth.EIGHT_B, requests=3, layers=2, kv_heads=2,
+                        q_heads=8, n_max=24, pool_blocks=3 * 24 + 2)
+    case = P.Case(spec)
+    wl, glob, host, dev, tables, dst, pinned, n_tok, _ = P.build_inputs(case)
+    zparams, _ = P._params_for(spec, 0)
+    pool = Z.make_pool(wl.k_pool, wl.v_pool)
+    R, L, H, b = spec.requests, spec.layers, spec.kv_heads, spec.block_size
+    U, k = R * L * H, spec.keep
+    out = Z.alloc_outputs(U, k, dev.n_cap, "cuda", debug=False)
+    ws = Z.alloc_workspace(pool, zparams, R, "cuda")
+    Z.zp_compress(pool, dev, wl.q_window, glob, zparams, out, ws)
+    q = synth.decode_queries(spec, R, "cuda", 5)
+    res = torch.full((R, L, spec.q_heads, spec.head_dim), float("nan"),
+                     dtype=torch.float32, device="cuda")
+    lens = torch.full((R,), k, dtype=torch.int32, device="cuda")
+    Z.zp_paged_decode(res, q, pool, dev.dst_table, lens, zparams)
+    torch.cuda.synchronize()
+    assert Z.zp_workspace_error(ws) == Z.ZP_OK
+    keep = out.keep_idx.cpu().numpy()
+    qh = synth.raw_numpy(q)
+    got = res.cpu().numpy().astype(np.float64)
+    G = spec.q_heads // H
+    for r in range(R):
+        for l in range(L):
+            for h in range(H):
+                u = (r * L + l) * H + h
+                keys = O.widen(O.gather_rows(host["k"], tables[r], l, h, spec.n_tokens, b),
+                               spec.dtype)[keep[u]]
+                vals = O.widen(O.gather_rows(host["v"], tables[r], l, h, spec.n_tokens, b),
+                               spec.dtype)[keep[u]]
+                want = O.decode_attention(O.widen(qh[r, l, h * G:(h + 1) * G], spec.dtype),
+                                          keys, vals)
+                err = np.abs(got[r, l, h * G:(h + 1) * G] - want)
+                assert np.all(err <= RTOL * np.abs(want) + ATOL), (r, l, h, err.max())
+
+
+def test_decode_rejects_bad_rows_on_device():
+    """A length beyond the table or a block id outside the pool makes the
+    kernel skip that unit (no output, no out-of-bounds read)."""
+    spec = DECODE_CASES[0][1]
+    dev = "cuda"
+    wl = synth.make(spec, device=dev)
+    R = spec.requests
+    tables = wl.tables.copy()
+    tables[1, 3] = spec.pool_blocks + 5        # request 1: id out of range
+    lens = np.full(R, spec.n_tokens, dtype=np.int32)
+    lens[2] = spec.n_tokens + 1                # request 2: needs a block more
+    lens[3] = 0                                # request 3: empty
+    q = synth.decode_queries(spec, R, dev, 3)
+    params = Z.make_params(spec.n_max, spec.window, spec.q_heads, Z.ZP_BF16)
+    out = torch.full((R, spec.layers, spec.q_heads, spec.head_dim), 123.0,
+                     dtype=torch.float32, device=dev)
+    Z.zp_paged_decode(out, q, Z.make_pool(wl.k_pool, wl.v_pool),
+                      torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev),
+                      params)
+    torch.cuda.synchronize()
+    o = out.cpu()
+    for r in (1, 2, 3):
+        assert bool((o[r] == 123.0).all()), f"request {r} was written"
+    assert bool(torch.isfinite(o[0]).all()) and not bool((o[0] == 123.0).any())

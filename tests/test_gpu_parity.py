@@ -77,6 +77,43 @@ def test_fp32_head_dim_128():
     _check(P.Case(F32_D128), "fp32 d=128")
 
 
+def test_long_context_takes_the_short_ring():
+    # 16384 tokens: the token rows (64 KiB) no longer fit beside the default
+    # 7-slot key ring in LDS, so the launcher picks the 4-slot ring
+    spec = synth.scaled(synth.EIGHT_B, requests=1, layers=1, kv_heads=2,
+                        q_heads=8, n_max=1024, pool_blocks=1024 + 8)
+    _check(P.Case(spec), "n = 16384 (4-slot ring)")
+
+
+def test_fp32_d128_n_cap_beyond_lds_is_rejected():
+    # fp32 keys with head_dim 128 take 8 KiB per block: token rows of 8192
+    # entries do not fit in LDS beside the ring; the call must refuse and
+    # leave every buffer untouched
+    spec = synth.scaled(F32_D128, requests=1, n_max=512, pool_blocks=512 + 4)
+    wl = synth.make(spec, device="cuda")
+    zparams, _ = P._params_for(spec, 0)
+    pool = Z.make_pool(wl.k_pool, wl.v_pool)
+    dev = "cuda"
+    batch = Z.DeviceBatch(
+        slot=torch.from_numpy(wl.slots).to(dev),
+        n_tokens=torch.from_numpy(wl.n_tokens).to(dev),
+        src_table=torch.from_numpy(wl.tables).to(dev),
+        dst_table=torch.from_numpy(wl.tables).to(dev),
+        n_pinned=torch.zeros(spec.requests, dtype=torch.int32, device=dev),
+        num_slots=spec.requests, n_cap=wl.n_cap)
+    U = spec.units
+    out = Z.alloc_outputs(U, spec.keep, wl.n_cap, dev, debug=True)
+    out.attn.fill_(7.0)
+    ws = Z.alloc_workspace(pool, zparams, spec.requests, dev)
+    k_before = wl.k_pool.clone()
+    with pytest.raises(Z.ZipageError) as ei:
+        Z.zp_compress(pool, batch, wl.q_window, wl.global_scores, zparams, out, ws)
+    assert ei.value.status == Z.ZP_EUNSUPPORTED
+    torch.cuda.synchronize()
+    assert bool((out.attn == 7.0).all())
+    assert torch.equal(k_before, wl.k_pool)
+
+
 def test_prefill_overshoot_ragged_tail():
     spec = synth.scaled(EIGHT_B, requests=3, pool_blocks=112 + 12)
     n = spec.n_tokens
@@ -238,3 +275,9 @@ def test_full_size_small_model_sampled():
 
 def test_full_size_8b_sampled():
     _full_size_sampled(synth.EIGHT_B, 6, 12)
+
+
+def test_full_size_prefix_sampled():
+    # 256 requests in 4 groups sharing 32 leading blocks each: the pinned
+    # prefix stays in place and the kept private rows go to fresh targets
+    _full_size_sampled(synth.PREFIX, 6, 13)
