@@ -14,6 +14,12 @@ GB/s of the whole step, a roofline entry for the dominant kernel (kernel
 durations from HIP events recorded on the launch stream during the timed
 steps) and the CPU oracle timed on a bounded sample of the same workload.
 
+With --workload overlap_512req_8grp the step is the two-stream case: 512
+requests in 8 groups, one group (64 requests, the query-slot holders) is
+compressed on stream C while the other 448 requests decode one token over all
+32 layers on stream D. Each step times C alone, D alone and both together;
+the line reports compressed tokens/s under overlap plus the three times.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        [--cpu-seconds S] [--no-cpu]
 """
@@ -152,6 +158,154 @@ def cpu_baseline(spec, wl, seconds: float) -> dict:
                       f"thread; a token covers {L * H} units"}
 
 
+def decode_bytes(spec, lens: np.ndarray) -> float:
+    """Algorithmic bytes of one decode call: K and V rows of every (request,
+    layer, KV head) read once, the query read and the fp32 output written."""
+    s = 2 if spec.dtype == "bf16" else 4
+    d, L, H, Hq = spec.head_dim, spec.layers, spec.kv_heads, spec.q_heads
+    R = lens.size
+    return (2.0 * s * d * float(lens.sum()) * L * H
+            + R * L * Hq * d * (s + 4))
+
+
+def run_overlap(args, spec):
+    """Compression of one group overlapped with decoding of the others."""
+    import torch
+    import kv_cache_compression_paged_amd as Z
+    from kv_cache_compression_paged_amd import synth
+    dev = "cuda"
+    groups = spec.compress_groups
+    per = spec.requests // groups
+    L, H = spec.layers, spec.kv_heads
+    n, k = spec.n_tokens, spec.keep
+    print(f"[bench] generating {spec.name} ({per} query slots)", file=sys.stderr,
+          flush=True)
+    t_gen = time.perf_counter()
+    wl = synth.make(spec, device=dev, slots=per)
+    torch.cuda.synchronize()
+    print(f"[bench] generated in {time.perf_counter() - t_gen:.1f} s",
+          file=sys.stderr, flush=True)
+    dt = Z.ZP_BF16 if spec.dtype == "bf16" else Z.ZP_F32
+    params = Z.make_params(spec.n_max, spec.window, spec.q_heads, dt)
+    pool = Z.make_pool(wl.k_pool, wl.v_pool)
+    Uc = per * L * H
+    out = Z.alloc_outputs(Uc, k, wl.n_cap, dev)
+    ws = Z.alloc_workspace(pool, params, per, dev)
+    R_d = spec.requests - per
+    q = torch.empty((R_d, L, spec.q_heads, spec.head_dim), dtype=wl.k_pool.dtype,
+                    device=dev)
+    dec = torch.empty((R_d, L, spec.q_heads, spec.head_dim), dtype=torch.float32,
+                      device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(spec.seed + 500)
+    rng = np.random.default_rng(spec.seed + 501)
+    sc, sd = torch.cuda.Stream(), torch.cuda.Stream()
+    steps, warm = args.steps, args.warmup
+    compressed = set()
+    rec = {"C": [], "D": [], "CD": [], "bytes_C": [], "bytes_D": []}
+
+    def elapsed(a, b):
+        return a.elapsed_time(b)
+
+    for i in range(warm + steps):
+        s = i % groups
+        grp = np.arange(s * per, (s + 1) * per)
+        rest = np.setdiff1d(np.arange(spec.requests), grp)
+        # A-23 lengths: groups compressed earlier decode at k, others at
+        # seeded lengths in [k+1, N-1]
+        lens = np.where(np.isin(rest // per, list(compressed)), k,
+                        rng.integers(k + 1, n, size=rest.size)).astype(np.int32)
+        tab_c = torch.from_numpy(np.ascontiguousarray(wl.tables[grp])).to(dev)
+        tab_d = torch.from_numpy(np.ascontiguousarray(wl.tables[rest])).to(dev)
+        lens_dev = torch.from_numpy(lens).to(dev)
+        batch = Z.DeviceBatch(
+            slot=torch.arange(per, dtype=torch.int32, device=dev),
+            n_tokens=torch.full((per,), n, dtype=torch.int32, device=dev),
+            src_table=tab_c, dst_table=tab_c.clone(),
+            n_pinned=torch.zeros(per, dtype=torch.int32, device=dev),
+            num_slots=per, n_cap=wl.n_cap)
+        holes = torch.empty((2, Uc), dtype=torch.int32, device=dev)
+        q.copy_(torch.randn(q.shape, generator=gen, device=dev))
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
+
+        def fresh_global(j):
+            # each compression of the group sees fresh U[0,1) global scores
+            wl.global_scores.copy_(torch.rand(wl.global_scores.shape, generator=gen,
+                                              device=dev))
+            torch.cuda.synchronize()
+            out.first_hole = holes[j]
+
+        # C alone
+        fresh_global(0)
+        ev[0].record(sc)
+        Z.zp_compress(pool, batch, wl.q_window, wl.global_scores, params, out, ws, sc)
+        Z.zp_update_global(wl.global_scores, pool, batch, out, params, sc)
+        ev[1].record(sc)
+        torch.cuda.synchronize()
+        # D alone
+        ev[2].record(sd)
+        Z.zp_paged_decode(dec, q, pool, tab_d, lens_dev, params, sd)
+        ev[3].record(sd)
+        torch.cuda.synchronize()
+        # both: D waits for C's start event, then the two run side by side
+        fresh_global(1)
+        ev[4].record(sc)
+        sd.wait_event(ev[4])
+        Z.zp_compress(pool, batch, wl.q_window, wl.global_scores, params, out, ws, sc)
+        Z.zp_update_global(wl.global_scores, pool, batch, out, params, sc)
+        Z.zp_paged_decode(dec, q, pool, tab_d, lens_dev, params, sd)
+        ev[5].record(sc)
+        ev[6].record(sd)
+        torch.cuda.synchronize()
+        if Z.zp_workspace_error(ws) != Z.ZP_OK:
+            raise RuntimeError("device error in the overlap step")
+        compressed.add(s)
+        if i < warm:
+            continue
+        hole_np = holes.cpu().numpy().astype(np.int64)
+        M = (k - hole_np).clip(min=0)
+        rec["C"].append(elapsed(ev[0], ev[1]))
+        rec["D"].append(elapsed(ev[2], ev[3]))
+        rec["CD"].append(max(elapsed(ev[4], ev[5]), elapsed(ev[4], ev[6])))
+        rec["bytes_C"].append(unit_bytes(spec, M[1])["step"])
+        rec["bytes_D"].append(decode_bytes(spec, lens))
+        print(f"[bench] step {i}: group {s} C {rec['C'][-1]:.2f} ms, D "
+              f"{rec['D'][-1]:.2f} ms, C||D {rec['CD'][-1]:.2f} ms",
+              file=sys.stderr, flush=True)
+    t_c, t_d, t_cd = (float(np.median(rec[x])) for x in ("C", "D", "CD"))
+    b_c, b_d = float(np.mean(rec["bytes_C"])), float(np.mean(rec["bytes_D"]))
+    ach = (b_c + b_d) / (t_cd * 1e-3) / 1e9
+    tokens = per * n
+    result = {
+        "metric": METRIC, "value": round(tokens / (t_cd * 1e-3), 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warm,
+        "ms_per_step": round(t_cd, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": spec.dtype,
+        "data": "synthetic",
+        "config": {"workload": spec.name, "requests": spec.requests,
+                   "groups": groups, "compressed_per_step": per,
+                   "decoded_per_step": spec.requests - per, "layers": L,
+                   "kv_heads": H, "q_heads": spec.q_heads,
+                   "head_dim": spec.head_dim, "n_max": spec.n_max,
+                   "tokens_per_request": n, "keep": k, "window": spec.window,
+                   "parallelism": "single GPU, two streams"},
+        "overlap": {"t_C_ms": round(t_c, 3), "t_D_ms": round(t_d, 3),
+                    "t_CD_ms": round(t_cd, 3),
+                    "gain": round((t_c + t_d) / t_cd, 3),
+                    "compress_GBps_alone": round(b_c / (t_c * 1e-3) / 1e9, 1),
+                    "decode_GBps_alone": round(b_d / (t_d * 1e-3) / 1e9, 1)},
+        "achieved_GBps": round(ach, 1),
+        "frac_of_peak": round(ach / HBM_PEAK_GBPS, 4),
+        "roofline": {"bound": "hbm", "kernel": "compress || decode",
+                     "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
+                     "traffic": None,
+                     "alg_bytes_per_launch": round(b_c + b_d)},
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -167,6 +321,9 @@ def main():
         sys.exit(1)
     Z.lib()
     spec = synth.SPECS[args.workload]
+    if spec.compress_groups > 1:
+        run_overlap(args, spec)
+        return
     dev = "cuda"
     print(f"[bench] generating {spec.name}", file=sys.stderr, flush=True)
     t_gen = time.perf_counter()

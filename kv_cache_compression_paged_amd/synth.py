@@ -116,24 +116,29 @@ def _normal_into(t: torch.Tensor, gen: torch.Generator, chunk_rows: int = 1
         t[i:i + chunk_rows].copy_(tmp)
 
 
-def _near_duplicates(k_layer: torch.Tensor, gen: torch.Generator) -> None:
+def _near_duplicates(k_layer: torch.Tensor, gen: torch.Generator,
+                     chunk: int = 1 << 17) -> None:
     """In every tile [block][head] of one layer, replace 5 of the b rows by a
-    noisy copy of another row of the same tile (the 11 others are sources)."""
+    noisy copy of another row of the same tile (the 11 others are sources).
+    Tiles are processed `chunk` at a time to bound the temporaries."""
     nb, hkv, b, d = k_layer.shape
     if b != 16:
         raise ValueError("near-duplicate recipe is defined for b = 16")
-    tiles = k_layer.view(nb * hkv, b, d)
-    order = torch.argsort(torch.rand((nb * hkv, b), generator=gen,
-                                     device=k_layer.device), dim=1)
-    dst = order[:, :5]
-    pick = torch.randint(0, 11, (nb * hkv, 5), generator=gen,
-                         device=k_layer.device)
-    src = torch.gather(order[:, 5:], 1, pick)
-    rows = torch.arange(nb * hkv, device=k_layer.device).unsqueeze(1)
-    noise = torch.randn((nb * hkv, 5, d), generator=gen,
-                        device=k_layer.device, dtype=torch.float32)
-    copies = tiles[rows, src].float() + 0.01 * noise
-    tiles[rows, dst] = copies.to(tiles.dtype)
+    all_tiles = k_layer.view(nb * hkv, b, d)
+    for c0 in range(0, nb * hkv, chunk):
+        tiles = all_tiles[c0:c0 + chunk]
+        nt = tiles.shape[0]
+        order = torch.argsort(torch.rand((nt, b), generator=gen,
+                                         device=k_layer.device), dim=1)
+        dst = order[:, :5]
+        pick = torch.randint(0, 11, (nt, 5), generator=gen,
+                             device=k_layer.device)
+        src = torch.gather(order[:, 5:], 1, pick)
+        rows = torch.arange(nt, device=k_layer.device).unsqueeze(1)
+        noise = torch.randn((nt, 5, d), generator=gen,
+                            device=k_layer.device, dtype=torch.float32)
+        copies = tiles[rows, src].float() + 0.01 * noise
+        tiles[rows, dst] = copies.to(tiles.dtype)
 
 
 def block_tables(spec: Spec) -> (np.ndarray, np.ndarray):

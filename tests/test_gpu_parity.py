@@ -166,76 +166,53 @@ def test_forced_ties_keep_prefix():
 
 # ------------------------------------------------------------ full size ---
 
-def _full_size_sampled(spec, n_samples, seed):
-    """Run the full call and check sampled units against the oracle."""
-    dev = "cuda"
-    _say(f"[full] generating {spec.name}")
-    wl = synth.make(spec, device=dev)
-    R, L, H, b = spec.requests, spec.layers, spec.kv_heads, spec.block_size
-    U = R * L * H
-    k, n = spec.keep, spec.n_tokens
-    rng = np.random.default_rng(seed)
-    units = sorted(set(int(x) for x in rng.choice(U, size=n_samples, replace=False)))
-    units = sorted(set(units) | {0, U - 1})
+def _save_units(spec, wl, tab_dev, units, slot_of=lambda r: r):
+    """Host copies of the sampled units' rows, window and global row."""
+    L, H = spec.layers, spec.kv_heads
+    n = spec.n_tokens
     G = spec.q_heads // H
-    tables = wl.tables
-    if spec.shared_blocks:
-        bm = Z.BlockManager(spec.pool_blocks)
-        bm.alloc(spec.pool_blocks)
-        for bid in range(spec.pool_blocks):
-            c = int(wl.refcount[bid])
-            if c == 0:
-                bm.release([bid])
-            for _ in range(c - 1):
-                bm.incref(bid)
-        plan = bm.plan_compress(tables, wl.n_tokens, spec.n_max, b)
-        dst, pinned = plan.dst_tables, plan.n_pinned
-    else:
-        dst, pinned = tables.copy(), np.zeros(R, dtype=np.int32)
-    tab_dev = torch.from_numpy(tables).to(dev)
     saved = {}
     for u in units:
         r, l, h = u // (L * H), (u // H) % L, u % H
         blocks = tab_dev[r].long()
         kr = wl.k_pool[l, blocks, h].reshape(n, -1)
         vr = wl.v_pool[l, blocks, h].reshape(n, -1)
+        sl = slot_of(r)
         saved[u] = (synth.raw_numpy(kr), synth.raw_numpy(vr),
-                    synth.raw_numpy(wl.q_window[r, l, :, h * G:(h + 1) * G]),
-                    wl.global_scores[r, l, h].cpu().numpy().copy())
-    zparams, oparams = P._params_for(spec, 0)
-    pool = Z.make_pool(wl.k_pool, wl.v_pool)
-    batch = Z.DeviceBatch(
-        slot=torch.from_numpy(wl.slots).to(dev),
-        n_tokens=torch.from_numpy(wl.n_tokens).to(dev),
-        src_table=tab_dev,
-        dst_table=torch.from_numpy(np.ascontiguousarray(dst, dtype=np.int32)).to(dev),
-        n_pinned=torch.from_numpy(np.ascontiguousarray(pinned, dtype=np.int32)).to(dev),
-        num_slots=R, n_cap=wl.n_cap)
-    out = Z.alloc_outputs(U, k, wl.n_cap, dev, debug=True)
-    ws = Z.alloc_workspace(pool, zparams, R, dev)
-    _say(f"[full] compress {spec.name}: U={U}")
-    Z.zp_compress(pool, batch, wl.q_window, wl.global_scores, zparams, out, ws)
-    Z.zp_update_global(wl.global_scores, pool, batch, out, zparams)
-    torch.cuda.synchronize()
-    assert Z.zp_workspace_error(ws) == Z.ZP_OK
-    # properties of every unit
+                    synth.raw_numpy(wl.q_window[sl, l, :, h * G:(h + 1) * G]),
+                    wl.global_scores[sl, l, h].cpu().numpy().copy())
+    return saved
+
+
+def _check_all_units(spec, out, glob_rows, shared):
+    """Properties that hold for every unit of the call."""
+    b, k, n = spec.block_size, spec.keep, spec.n_tokens
     keep = out.keep_idx
     assert bool((keep[:, 1:] > keep[:, :-1]).all()), "keep rows not ascending"
     assert int(keep.min()) >= 0 and int(keep.max()) < n
-    if not spec.shared_blocks:
-        ar = torch.arange(k, device=dev, dtype=torch.int32)
+    if not shared:
+        ar = torch.arange(k, device=keep.device, dtype=torch.int32)
         hole_ref = torch.where(keep != ar, ar, torch.full_like(ar, k)).min(dim=1).values
         assert torch.equal(hole_ref, out.first_hole)
     else:
         assert bool((keep[:, :spec.shared_blocks * b] ==
-                     torch.arange(spec.shared_blocks * b, device=dev,
+                     torch.arange(spec.shared_blocks * b, device=keep.device,
                                   dtype=torch.int32)).all())
-    tail = wl.global_scores[..., k:]
+    tail = glob_rows[..., k:]
     assert bool((tail == 0).all()), "global tail not zeroed"
-    dst_dev = batch.dst_table
-    for u in units:
+
+
+def _check_sampled_units(spec, wl, out, saved, pinned, dst_dev, unit_base=0,
+                         slot_of=lambda r: r):
+    """Sampled units one by one against the oracle. `saved` is keyed by the
+    unit's index in the call; unit_base offsets the request index into the
+    workload's tables and pools."""
+    L, H, b = spec.layers, spec.kv_heads, spec.block_size
+    k, n = spec.keep, spec.n_tokens
+    _, oparams = P._params_for(spec, 0)
+    keep = out.keep_idx
+    for u, (kr, vr, q, g) in saved.items():
         r, l, h = u // (L * H), (u // H) % L, u % H
-        kr, vr, q, g = saved[u]
         keys = O.widen(kr, spec.dtype)
         ur = O.score_unit(O.widen(q, spec.dtype), keys, g.astype(np.float64), n,
                           int(pinned[r]), oparams)
@@ -261,9 +238,60 @@ def _full_size_sampled(spec, n_samples, seed):
         assert nv[:k].tobytes() == vr[gk].tobytes(), f"V rows of unit {u}"
         if not spec.shared_blocks:  # the tail block keeps its old rows
             assert nk[k:].tobytes() == kr[k:n].tobytes()
-        gn = wl.global_scores[r, l, h].cpu().numpy().astype(np.float64)
+        gn = wl.global_scores[slot_of(r), l, h].cpu().numpy().astype(np.float64)
         gref = O.update_global(g, ur.attn, gk, k)
         assert np.all(np.abs(gn - gref) <= 1e-4 * np.abs(gref) + 1e-6)
+
+
+def _sample_units(U, n_samples, seed):
+    rng = np.random.default_rng(seed)
+    units = set(int(x) for x in rng.choice(U, size=n_samples, replace=False))
+    return sorted(units | {0, U - 1})
+
+
+def _full_size_sampled(spec, n_samples, seed):
+    """Run the full call and check sampled units against the oracle."""
+    dev = "cuda"
+    _say(f"[full] generating {spec.name}")
+    wl = synth.make(spec, device=dev)
+    R, L, H, b = spec.requests, spec.layers, spec.kv_heads, spec.block_size
+    U = R * L * H
+    k = spec.keep
+    units = _sample_units(U, n_samples, seed)
+    tables = wl.tables
+    if spec.shared_blocks:
+        bm = Z.BlockManager(spec.pool_blocks)
+        bm.alloc(spec.pool_blocks)
+        for bid in range(spec.pool_blocks):
+            c = int(wl.refcount[bid])
+            if c == 0:
+                bm.release([bid])
+            for _ in range(c - 1):
+                bm.incref(bid)
+        plan = bm.plan_compress(tables, wl.n_tokens, spec.n_max, b)
+        dst, pinned = plan.dst_tables, plan.n_pinned
+    else:
+        dst, pinned = tables.copy(), np.zeros(R, dtype=np.int32)
+    tab_dev = torch.from_numpy(tables).to(dev)
+    saved = _save_units(spec, wl, tab_dev, units)
+    zparams, _ = P._params_for(spec, 0)
+    pool = Z.make_pool(wl.k_pool, wl.v_pool)
+    batch = Z.DeviceBatch(
+        slot=torch.from_numpy(wl.slots).to(dev),
+        n_tokens=torch.from_numpy(wl.n_tokens).to(dev),
+        src_table=tab_dev,
+        dst_table=torch.from_numpy(np.ascontiguousarray(dst, dtype=np.int32)).to(dev),
+        n_pinned=torch.from_numpy(np.ascontiguousarray(pinned, dtype=np.int32)).to(dev),
+        num_slots=R, n_cap=wl.n_cap)
+    out = Z.alloc_outputs(U, k, wl.n_cap, dev, debug=True)
+    ws = Z.alloc_workspace(pool, zparams, R, dev)
+    _say(f"[full] compress {spec.name}: U={U}")
+    Z.zp_compress(pool, batch, wl.q_window, wl.global_scores, zparams, out, ws)
+    Z.zp_update_global(wl.global_scores, pool, batch, out, zparams)
+    torch.cuda.synchronize()
+    assert Z.zp_workspace_error(ws) == Z.ZP_OK
+    _check_all_units(spec, out, wl.global_scores, bool(spec.shared_blocks))
+    _check_sampled_units(spec, wl, out, saved, pinned, batch.dst_table)
     _say(f"[full] {spec.name}: {len(units)} sampled units match")
     del wl, out
     torch.cuda.empty_cache()
@@ -281,3 +309,75 @@ def test_full_size_prefix_sampled():
     # 256 requests in 4 groups sharing 32 leading blocks each: the pinned
     # prefix stays in place and the kept private rows go to fresh targets
     _full_size_sampled(synth.PREFIX, 6, 13)
+
+
+def test_full_size_overlap_sampled():
+    """512 requests in 8 groups: group 0 (64 requests, all 32 layers, holding
+    the query slots) is compressed on one stream while the other 448 requests
+    decode on a second stream. Sampled compressed units and sampled decode
+    (request, layer) pairs are checked against the oracle."""
+    spec = synth.OVERLAP
+    dev = "cuda"
+    per = spec.requests // spec.compress_groups
+    _say(f"[full] generating {spec.name} ({per} query slots)")
+    wl = synth.make(spec, device=dev, slots=per)
+    L, H = spec.layers, spec.kv_heads
+    n, k = spec.n_tokens, spec.keep
+    tables = wl.tables
+    grp = np.arange(per)
+    rest = np.arange(per, spec.requests)
+    tab_c = torch.from_numpy(np.ascontiguousarray(tables[grp])).to(dev)
+    tab_d = torch.from_numpy(np.ascontiguousarray(tables[rest])).to(dev)
+    Uc = per * L * H
+    units = _sample_units(Uc, 6, 14)
+    saved = _save_units(spec, wl, tab_c, units)
+    rng = np.random.default_rng(spec.seed + 3)
+    lens = rng.integers(k + 1, n, size=rest.size).astype(np.int32)  # U{k+1..N-1}
+    q = synth.decode_queries(spec, rest.size, dev, spec.seed + 4)
+    zparams, _ = P._params_for(spec, 0)
+    pool = Z.make_pool(wl.k_pool, wl.v_pool)
+    batch = Z.DeviceBatch(
+        slot=torch.arange(per, dtype=torch.int32, device=dev),
+        n_tokens=torch.full((per,), n, dtype=torch.int32, device=dev),
+        src_table=tab_c, dst_table=tab_c.clone(),
+        n_pinned=torch.zeros(per, dtype=torch.int32, device=dev),
+        num_slots=per, n_cap=wl.n_cap)
+    out = Z.alloc_outputs(Uc, k, wl.n_cap, dev, debug=True)
+    ws = Z.alloc_workspace(pool, zparams, per, dev)
+    dec = torch.full((rest.size, L, spec.q_heads, spec.head_dim), float("nan"),
+                     dtype=torch.float32, device=dev)
+    lens_dev = torch.from_numpy(lens).to(dev)
+    sc, sd = torch.cuda.Stream(), torch.cuda.Stream()
+    ready = torch.cuda.Event()
+    ready.record(torch.cuda.current_stream())
+    sc.wait_event(ready)
+    sd.wait_event(ready)
+    _say(f"[full] compress {Uc} units on stream C, decode {rest.size} requests on stream D")
+    Z.zp_compress(pool, batch, wl.q_window, wl.global_scores, zparams, out, ws, sc)
+    Z.zp_update_global(wl.global_scores, pool, batch, out, zparams, sc)
+    Z.zp_paged_decode(dec, q, pool, tab_d, lens_dev, zparams, sd)
+    torch.cuda.synchronize()
+    assert Z.zp_workspace_error(ws) == Z.ZP_OK
+    _check_all_units(spec, out, wl.global_scores, False)
+    _check_sampled_units(spec, wl, out, saved, np.zeros(per, dtype=np.int32),
+                         batch.dst_table)
+    _say(f"[full] {spec.name}: {len(units)} sampled compressed units match")
+    # decode: 64 seeded (request, layer) pairs of the other groups
+    pairs = sorted(set((int(a), int(b)) for a, b in zip(
+        rng.integers(0, rest.size, 64), rng.integers(0, L, 64))))
+    qh = synth.raw_numpy(q)
+    got = dec.cpu().numpy().astype(np.float64)
+    G = spec.q_heads // H
+    for (i, l) in pairs:
+        r = int(rest[i])
+        blocks = torch.from_numpy(tables[r]).to(dev).long()
+        for h in range(H):
+            kr = synth.raw_numpy(wl.k_pool[l, blocks, h].reshape(n, -1))[:lens[i]]
+            vr = synth.raw_numpy(wl.v_pool[l, blocks, h].reshape(n, -1))[:lens[i]]
+            want = O.decode_attention(O.widen(qh[i, l, h * G:(h + 1) * G], spec.dtype),
+                                      O.widen(kr, spec.dtype), O.widen(vr, spec.dtype))
+            err = np.abs(got[i, l, h * G:(h + 1) * G] - want)
+            assert np.all(err <= 1e-4 * np.abs(want) + 1e-5), (r, l, h, err.max())
+    _say(f"[full] {spec.name}: {len(pairs)} sampled decode pairs match")
+    del wl, out, dec
+    torch.cuda.empty_cache()
