@@ -1,7 +1,7 @@
 """Throughput of the Compressed-PagedAttention compression step on one GPU.
 
-A step is one whole compression pass over the batch: zp_compress (score +
-select, then K/V compaction) followed by zp_update_global, for every
+A step is one whole compression pass over the batch: zp_compress (score,
+select and K/V compaction in one kernel) followed by zp_update_global, for every
 (request, layer, KV head) unit of the workload. The default workload is the
 8B-like shape: 128 requests x 32 layers x 8 KV heads (32 query heads),
 head_dim 128, b = 16, N_max = 256 (4096 tokens, keep 4080), w = 32, bf16
@@ -61,9 +61,9 @@ def unit_bytes(spec, M: np.ndarray) -> dict:
     whole step: s*d*(N + 4M) + s_q*w*G*d + 12*N_cap (keys read once, moved K
     and V rows read and written, the window, global read for scoring plus the
     read and write of the update); per kernel:
-      score_select: s*d*N + s_q*w*G*d + 4N (global) + 4N (attn out) + 4k (keep)
-      compact:      4*M*d*s + 4*M (keep entries of moved rows)
-      global:       8*N_cap + 8k (row read/write, keep and attn at kept)
+      compress: s*d*N + s_q*w*G*d + 4N (global) + 4N (attn out) + 4k (keep)
+                + 4*M*d*s (moved K and V rows, read and written)
+      global:   8*N_cap + 8k (row read/write, keep and attn at kept)
     """
     s = 2 if spec.dtype == "bf16" else 4
     d, N, k = spec.head_dim, spec.n_tokens, spec.keep
@@ -74,16 +74,14 @@ def unit_bytes(spec, M: np.ndarray) -> dict:
     Msum = float(M.sum())
     return {
         "step": U * (s * d * N + wGd + 12 * n_cap) + 4.0 * s * d * Msum,
-        "score_select": U * (s * d * N + wGd + 4 * N + 4 * N + 4 * k),
-        "compact": 4.0 * s * d * Msum + 4.0 * Msum,
+        "compress": U * (s * d * N + wGd + 4 * N + 4 * N + 4 * k) + 4.0 * s * d * Msum,
         "global_update": U * (8 * n_cap + 8 * k),
     }
 
 
 KERNEL_SOURCES = {
-    "score_select": ["score_select.hip", "zp_device.h"],
-    "compact": ["compact.hip", "zp_device.h"],
-    "global_update": ["compact.hip", "zp_device.h"],
+    "compress": ["compress.hip", "zp_device.h"],
+    "global_update": ["global_update.hip", "zp_device.h"],
 }
 
 

@@ -22,7 +22,8 @@
  *   - Device tables are checked by the kernels as they read them: a block id
  *     outside [0, num_blocks), a token count outside its allowed range or a
  *     slot outside [0, num_slots) makes the affected (request, layer, head)
- *     unit skip all memory writes and records ZP_EDEVICE in the workspace.
+ *     unit skip all memory writes except first_hole[u] = -1 (when that output
+ *     is requested) and records ZP_EDEVICE in the workspace.
  *   - No C++ exception crosses this interface.
  */
 #ifndef ZIPAGE_H
@@ -140,7 +141,8 @@ typedef struct {
   int32_t* first_hole;
 } zp_compress_out;
 
-/* Bytes of device workspace zp_compress needs for num_reqs requests.
+/* Bytes of device workspace zp_compress needs for num_reqs requests (256:
+ * the device error word and padding, whatever the batch).
  * Errors: ZP_EINVAL for a NULL argument or non-positive sizes. */
 zp_status zp_compress_workspace_bytes(const zp_kv_pool* pool,
                                       const zp_params* params,
@@ -265,11 +267,10 @@ int32_t zp_plan_targets(const zp_plan* plan, int32_t* ids, int32_t cap);
  * the recorded events, and returns per kernel kind the launch count and the
  * summed milliseconds, then clears the record.
  * ------------------------------------------------------------------------ */
-#define ZP_KERNEL_SCORE   0   /* score + select                              */
-#define ZP_KERNEL_COMPACT 1   /* K/V row compaction                          */
-#define ZP_KERNEL_GLOBAL  2   /* global-score update                         */
-#define ZP_KERNEL_DECODE  3   /* paged decode                                */
-#define ZP_KERNEL_KINDS   4
+#define ZP_KERNEL_COMPRESS 0  /* score, select and K/V compaction            */
+#define ZP_KERNEL_GLOBAL   1  /* global-score update                         */
+#define ZP_KERNEL_DECODE   2  /* paged decode                                */
+#define ZP_KERNEL_KINDS    3
 
 zp_status zp_timing_enable(int32_t enable);
 zp_status zp_timing_read(int32_t* launches /*[ZP_KERNEL_KINDS]*/,

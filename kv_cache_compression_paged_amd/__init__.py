@@ -36,12 +36,11 @@ ZP_BF16 = 1
 ZP_NONCAUSAL = 1 << 0
 ZP_PROTECT_WINDOW = 1 << 1
 
-ZP_KERNEL_SCORE = 0
-ZP_KERNEL_COMPACT = 1
-ZP_KERNEL_GLOBAL = 2
-ZP_KERNEL_DECODE = 3
-ZP_KERNEL_KINDS = 4
-KERNEL_NAMES = ("score_select", "compact", "global_update", "paged_decode")
+ZP_KERNEL_COMPRESS = 0
+ZP_KERNEL_GLOBAL = 1
+ZP_KERNEL_DECODE = 2
+ZP_KERNEL_KINDS = 3
+KERNEL_NAMES = ("compress", "global_update", "paged_decode")
 
 EXPORTED = (
     "zp_compress_workspace_bytes", "zp_compress", "zp_update_global",

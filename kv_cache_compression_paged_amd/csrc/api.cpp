@@ -170,7 +170,8 @@ zp_status make_geom(const zp_kv_pool* pool, const zp_params* p,
 constexpr size_t kWsHeader = 256;
 
 size_t workspace_for(int64_t units) {
-  return kWsHeader + ((static_cast<size_t>(units) * sizeof(int32_t) + 255) & ~size_t(255));
+  (void)units;
+  return kWsHeader;
 }
 
 }  // namespace
@@ -211,16 +212,9 @@ zp_status zp_compress(const zp_kv_pool* pool, const zp_batch* batch,
                 workspace_bytes, workspace_for(units));
   if (g.R == 0) return ZP_OK;
   int32_t* err = static_cast<int32_t*>(workspace);
-  int32_t* hole = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + kWsHeader);
-
-  timing_before(ZP_KERNEL_SCORE, stream);
-  st = launch_score_select(g, *pool, *batch, q_window, global_scores, *out, hole,
-                           err, stream);
-  timing_after(ZP_KERNEL_SCORE, stream);
-  if (st != ZP_OK) return st;
-  timing_before(ZP_KERNEL_COMPACT, stream);
-  st = launch_compact(g, *pool, *batch, out->keep_idx, hole, err, stream);
-  timing_after(ZP_KERNEL_COMPACT, stream);
+  timing_before(ZP_KERNEL_COMPRESS, stream);
+  st = launch_compress(g, *pool, *batch, q_window, global_scores, *out, err, stream);
+  timing_after(ZP_KERNEL_COMPRESS, stream);
   return st;
 }
 

@@ -1,5 +1,5 @@
-// Score and select kernel: one workgroup of 8 waves per (request, layer, KV
-// head) unit.
+// Compression kernel: one workgroup of 8 waves per (request, layer, KV head)
+// unit scores, selects and compacts that unit.
 //
 // Steps, in the order of the method ([zh] §2.1, [de] §2, [es] §2):
 //   phase 1  sweep the unit's keys once through the block table: window
@@ -14,7 +14,12 @@
 //   select   keep the k = (N_max-1) b best tokens of the unit ([zh] §2.1):
 //            an exact radix select on order-preserving 32-bit score keys,
 //            ties broken toward the lower position, then the kept positions
-//            are written ascending together with the first evicted one.
+//            are written ascending together with the first evicted one;
+//   compact  move the kept K and V rows, in order, to logical rows [0, k)
+//            through the destination table ([zh] §2.1, §2.2).
+// Compaction runs in the same workgroup right after its select, so while
+// one CU streams its unit's rows other CUs are in their MFMA/exp sweeps: the
+// copy traffic overlaps the scoring work instead of following it.
 //
 // Organisation (gfx950). Wave w is (key quarter kq = w % 4, row half
 // rg = w / 4): at step s the two waves of quarter kq handle key block
@@ -30,7 +35,8 @@
 // wave's own loads plus a raw s_barrier (a __syncthreads would drain every
 // load in flight). Two waves share a SIMD, so one's MFMA overlaps the
 // other's exp/VALU work. Long contexts (token rows that do not fit beside
-// the default ring in LDS) take a 4-slot ring.
+// the default ring in LDS) take a 4-slot ring. The column sweep runs
+// backward so it starts on the blocks the first sweep read last.
 #include <hip/hip_runtime.h>
 
 #include "zp_device.h"
@@ -49,7 +55,8 @@ constexpr int kQuarters = 4;
 constexpr int kB = 16;  // block size b (one key tile = one block)
 
 struct ScoreArgs {
-  const void* kpool;
+  void* kpool;
+  void* vpool;
   const void* q_window;
   const float* glob;
   const int32_t* slot;
@@ -61,7 +68,6 @@ struct ScoreArgs {
   float* attn;
   float* red;
   float* score;
-  int32_t* hole;
   int32_t* hole_out;
   int32_t* err;
   int32_t L, NB, Hkv, Hq, G, w, wG, n_cap, num_slots, max_blocks, n_max, k;
@@ -126,7 +132,7 @@ struct TileGeom {
 };
 
 template <typename E, int D, int RT, int NS>
-__global__ __launch_bounds__(kThreads) void score_select_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(kThreads) void compress_kernel(ScoreArgs a) {
   using FragT = Frag<E, D>;
   using TG = TileGeom<E, D, NS>;
   constexpr int kRows = RT * 16;
@@ -185,7 +191,7 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(ScoreArgs a) {
   }
   if (__syncthreads_or(bad)) {
     if (tid == 0) {
-      a.hole[u] = -1;
+      if (a.hole_out) a.hole_out[u] = -1;
       *a.err = ZP_EDEVICE;
     }
     return;
@@ -217,7 +223,12 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(ScoreArgs a) {
 
   const float sl2 = a.sl2;
   const int nsteps = (nt + kQuarters - 1) / kQuarters;
-  auto tile_of = [&](int s) { return s * kQuarters + kq; };
+  // Sweeps run forward or backward over a quarter's blocks; the backward
+  // column sweep starts with the blocks the row-statistics sweep read last,
+  // while they may still sit in the caches.
+  bool backward = false;
+  int last_q = 0;  // last step with a block for this quarter (set below)
+  auto tile_of = [&](int s) { return (backward ? last_q - s : s) * kQuarters + kq; };
   auto tile_masked = [&](int kt) {
     return (kt + 1) * kB > n || (causal && kt * kB + kB - 1 > n - a.w);
   };
@@ -241,6 +252,7 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(ScoreArgs a) {
     frag_off[c] = TG::chunk_off(nl, jg * FragT::kChunks + c);
   // last step that has a block for this quarter (-1: none)
   const int last = kq < nt ? (nt - 1 - kq) / kQuarters : -1;
+  last_q = last;
   struct Acc {
     f32x4_t a[RTW];
     f32x4_t g;
@@ -494,6 +506,7 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(ScoreArgs a) {
     const int t = tile_of(s) * kB + nl;
     if (t < n) a.attn[urow + t] = (cs + xchg[kq][s & 3][nl]) * inv_rows;
   };
+  backward = true;
   sweep([&](const FragT& kc, int, Acc& acc) { logits(kc, acc, false); },
         [&](const Acc& acc, int kt, int s) {
     const int t = kt * kB + nl;
@@ -618,21 +631,70 @@ __global__ __launch_bounds__(kThreads) void score_select_kernel(ScoreArgs a) {
   }
   int kept_total;
   const int off = zpd::block_exclusive_scan<kWaves>(kept, scratch, &kept_total);
+  const int hole = zpd::block_min<kWaves>(first_ev, scratch);
+  if (kept_total != a.k) {  // cannot happen for a consistent unit
+    if (tid == 0) *a.err = ZP_EDEVICE;
+    if (tid == 0 && a.hole_out) a.hole_out[u] = -1;
+    return;
+  }
+  // kept positions, ascending: to the output row and (the keys are no longer
+  // read: both scans above passed barriers) to LDS for the compaction
   int32_t* keep_row = a.keep + static_cast<int64_t>(u) * a.k;
-  if (kept_total == a.k) {
+  int* keep_l = reinterpret_cast<int*>(s_tok);
+  {
     int o = off;
     for (int t = t0; t < t1; ++t)
-      if (!((evict >> (t - t0)) & 1ull)) keep_row[o++] = t;
+      if (!((evict >> (t - t0)) & 1ull)) {
+        keep_row[o] = t;
+        keep_l[o++] = t;
+      }
   }
-  const int hole = zpd::block_min<kWaves>(first_ev, scratch);
-  if (tid == 0) {
-    if (kept_total != a.k) {  // cannot happen for a consistent unit
-      a.hole[u] = -1;
-      *a.err = ZP_EDEVICE;
-    } else {
-      a.hole[u] = hole;
-      if (a.hole_out) a.hole_out[u] = hole;
+  if (tid == 0 && a.hole_out) a.hole_out[u] = hole;
+
+  // ---- compaction: kept K and V rows, in order, to logical rows [0, k)
+  // ([zh] §2.1 re-packing into the first N_max-1 blocks; [zh] §2.2 target
+  // blocks after a shared prefix). In place the source of row t is
+  // keep[t] >= t and rows below the first hole already hold their token.
+  // Rows [start, k) go in ascending chunks; every lane finishes all loads of
+  // a chunk before any lane stores it, and a later chunk only reads rows at
+  // or above its own start, so no row is overwritten before it is read. With
+  // a shared prefix the destinations are fresh target blocks.
+  const int start = S > 0 ? S * kB : hole;
+  int* dtab = reinterpret_cast<int*>(&ring[0][0][0]);  // the ring is idle
+  for (int j = tid; j < a.n_max; j += kThreads) dtab[j] = dst_tab[j];
+  __syncthreads();
+  if (start >= a.k) return;
+  constexpr int kPieces = TG::kRowChunks;               // 16-byte pieces per row
+  constexpr int kRowsPerPass = kThreads / kPieces;
+  constexpr int kPasses = 8;
+  constexpr int kRowsPerChunk = kRowsPerPass * kPasses;
+  char* kmut = static_cast<char*>(a.kpool) +
+               (static_cast<int64_t>(l) * a.NB * a.Hkv + h) * TG::kTileBytes;
+  char* vmut = static_cast<char*>(a.vpool) +
+               (static_cast<int64_t>(l) * a.NB * a.Hkv + h) * TG::kTileBytes;
+  const int piece16 = (tid % kPieces) * 16, prow = tid / kPieces;
+  const int k = a.k;
+  for (int c0 = start; c0 < k; c0 += kRowsPerChunk) {
+    zpd::u32x4_t vk[kPasses], vv[kPasses];
+    int64_t doff[kPasses];
+    // rows past k are clamped to row k-1 (always valid) and not stored
+#pragma unroll
+    for (int e = 0; e < kPasses; ++e) {
+      const int t = min(c0 + e * kRowsPerPass + prow, k - 1);
+      const int sp = keep_l[t];
+      const int64_t soff = tab[sp / kB] * block_stride + (sp % kB) * TG::kRowBytes + piece16;
+      vk[e] = *reinterpret_cast<const zpd::u32x4_t*>(kmut + soff);
+      vv[e] = *reinterpret_cast<const zpd::u32x4_t*>(vmut + soff);
+      doff[e] = dtab[t / kB] * block_stride + (t % kB) * TG::kRowBytes + piece16;
     }
+    zpd::wait_all_memory();
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < kPasses; ++e)
+      if (c0 + e * kRowsPerPass + prow < k) {
+        *reinterpret_cast<zpd::u32x4_t*>(kmut + doff[e]) = vk[e];
+        *reinterpret_cast<zpd::u32x4_t*>(vmut + doff[e]) = vv[e];
+      }
   }
 }
 
@@ -640,7 +702,7 @@ template <typename E, int D, int RT, int NS>
 zp_status launch_one(const zp::CompressGeom& g, const ScoreArgs& args,
                      void* stream) {
   const size_t dyn = static_cast<size_t>(g.n_cap) * sizeof(float);
-  auto kern = score_select_kernel<E, D, RT, NS>;
+  auto kern = compress_kernel<E, D, RT, NS>;
   hipFuncAttributes fa;
   hipError_t e = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(kern));
   if (e != hipSuccess)
@@ -671,7 +733,7 @@ zp_status launch_ring(const zp::CompressGeom& g, const ScoreArgs& args,
   if constexpr (ns > kLongSlots) {
     hipFuncAttributes fa;
     const hipError_t e = hipFuncGetAttributes(
-        &fa, reinterpret_cast<const void*>(score_select_kernel<E, D, RT, ns>));
+        &fa, reinterpret_cast<const void*>(compress_kernel<E, D, RT, ns>));
     if (e != hipSuccess)
       return zp::fail(ZP_EHIP, "score kernel attributes: %s", hipGetErrorString(e));
     if (fa.sharedSizeBytes + static_cast<size_t>(g.n_cap) * sizeof(float) > 160 * 1024)
@@ -705,13 +767,13 @@ zp_status dispatch_rows(const zp::CompressGeom& g, const ScoreArgs& args,
 
 namespace zp {
 
-zp_status launch_score_select(const CompressGeom& g, const zp_kv_pool& pool,
-                              const zp_batch& batch, const void* q_window,
-                              const float* global_scores,
-                              const zp_compress_out& out, int32_t* hole,
-                              int32_t* err, void* stream) {
+zp_status launch_compress(const CompressGeom& g, const zp_kv_pool& pool,
+                          const zp_batch& batch, const void* q_window,
+                          const float* global_scores,
+                          const zp_compress_out& out, int32_t* err, void* stream) {
   ScoreArgs a;
   a.kpool = pool.k;
+  a.vpool = pool.v;
   a.q_window = q_window;
   a.glob = global_scores;
   a.slot = batch.slot;
@@ -723,7 +785,6 @@ zp_status launch_score_select(const CompressGeom& g, const zp_kv_pool& pool,
   a.attn = out.attn;
   a.red = out.red;
   a.score = out.score;
-  a.hole = hole;
   a.hole_out = out.first_hole;
   a.err = err;
   a.L = g.L;

@@ -26,14 +26,10 @@ struct CompressGeom {
 
 // Launchers (defined next to their kernels). Each returns ZP_OK or ZP_EHIP
 // (launch error), after recording the error text.
-zp_status launch_score_select(const CompressGeom& g, const zp_kv_pool& pool,
-                              const zp_batch& batch, const void* q_window,
-                              const float* global_scores,
-                              const zp_compress_out& out, int32_t* hole,
-                              int32_t* err, void* stream);
-zp_status launch_compact(const CompressGeom& g, const zp_kv_pool& pool,
-                         const zp_batch& batch, const int32_t* keep,
-                         const int32_t* hole, int32_t* err, void* stream);
+zp_status launch_compress(const CompressGeom& g, const zp_kv_pool& pool,
+                          const zp_batch& batch, const void* q_window,
+                          const float* global_scores,
+                          const zp_compress_out& out, int32_t* err, void* stream);
 zp_status launch_global(const CompressGeom& g, float* global_scores,
                         const zp_batch& batch, const int32_t* keep,
                         const float* attn, void* stream);
