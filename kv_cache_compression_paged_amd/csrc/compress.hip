@@ -658,7 +658,10 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(ScoreArgs a) {
   // Rows [start, k) go in ascending chunks; every lane finishes all loads of
   // a chunk before any lane stores it, and a later chunk only reads rows at
   // or above its own start, so no row is overwritten before it is read. With
-  // a shared prefix the destinations are fresh target blocks.
+  // a shared prefix the destinations are fresh target blocks. The copy is
+  // streamed with nontemporal loads and stores: its rows are touched once,
+  // and keeping them out of the caches leaves those to the key sweeps of the
+  // units other CUs are scoring.
   const int start = S > 0 ? S * kB : hole;
   int* dtab = reinterpret_cast<int*>(&ring[0][0][0]);  // the ring is idle
   for (int j = tid; j < a.n_max; j += kThreads) dtab[j] = dst_tab[j];
@@ -683,8 +686,8 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(ScoreArgs a) {
       const int t = min(c0 + e * kRowsPerPass + prow, k - 1);
       const int sp = keep_l[t];
       const int64_t soff = tab[sp / kB] * block_stride + (sp % kB) * TG::kRowBytes + piece16;
-      vk[e] = *reinterpret_cast<const zpd::u32x4_t*>(kmut + soff);
-      vv[e] = *reinterpret_cast<const zpd::u32x4_t*>(vmut + soff);
+      vk[e] = __builtin_nontemporal_load(reinterpret_cast<const zpd::u32x4_t*>(kmut + soff));
+      vv[e] = __builtin_nontemporal_load(reinterpret_cast<const zpd::u32x4_t*>(vmut + soff));
       doff[e] = dtab[t / kB] * block_stride + (t % kB) * TG::kRowBytes + piece16;
     }
     zpd::wait_all_memory();
@@ -692,8 +695,8 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(ScoreArgs a) {
 #pragma unroll
     for (int e = 0; e < kPasses; ++e)
       if (c0 + e * kRowsPerPass + prow < k) {
-        *reinterpret_cast<zpd::u32x4_t*>(kmut + doff[e]) = vk[e];
-        *reinterpret_cast<zpd::u32x4_t*>(vmut + doff[e]) = vv[e];
+        __builtin_nontemporal_store(vk[e], reinterpret_cast<zpd::u32x4_t*>(kmut + doff[e]));
+        __builtin_nontemporal_store(vv[e], reinterpret_cast<zpd::u32x4_t*>(vmut + doff[e]));
       }
   }
 }
