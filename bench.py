@@ -357,6 +357,18 @@ def main():
     for _ in range(warm + steps - 1):
         globs.append(torch.rand(wl.global_scores.shape, generator=gen,
                                 device=dev, dtype=torch.float32))
+    # the box's own copy rate: a plain 2 GiB device-to-device copy
+    csrc = torch.empty(1 << 29, dtype=torch.float32, device=dev).fill_(1.0)
+    cdst = torch.empty_like(csrc)
+    cdst.copy_(csrc)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        cdst.copy_(csrc)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 5 * 2 * csrc.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del csrc, cdst
     if args.copy_calibration:
         # a plain copy of known size, for scaling the HBM byte counters
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
@@ -409,11 +421,23 @@ def main():
                          "alg_GBps": round(b / (avg * 1e-3) / 1e9, 1) if b else None}
     dom = max(kernels, key=lambda x: kernels[x]["avg_ms"] * kernels[x]["launches"])
     dom_ach = kernels[dom]["alg_GBps"]
+    traffic = traffic_from_profile(dom, spec)
     roofline = {"bound": "hbm", "kernel": dom, "achieved": dom_ach,
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(dom_ach / HBM_PEAK_GBPS, 4),
-                "traffic": traffic_from_profile(dom, spec),
-                "alg_bytes_per_launch": round(alg[dom])}
+                "traffic": traffic,
+                "alg_bytes_per_launch": round(alg[dom]),
+                "traffic_GBps": (round(traffic / (kernels[dom]["avg_ms"] * 1e-3) / 1e9, 1)
+                                 if traffic else None)}
+    # MFMA work of the scoring (window logits + block Grams, counted once):
+    # 2*w*G*d*N + 2*b*d*N flops per unit
+    G = spec.q_heads // spec.kv_heads
+    flops = U * (2.0 * spec.window * G * spec.head_dim * n
+                 + 2.0 * spec.block_size * spec.head_dim * n)
+    t_c = kernels["compress"]["avg_ms"] * 1e-3
+    mfma = {"alg_TFLOPs": round(flops / t_c / 1e12, 1),
+            "peak_TFLOPs": 2500.0 if spec.dtype == "bf16" else 157.3,
+            "frac": round(flops / t_c / 1e12 / (2500.0 if spec.dtype == "bf16" else 157.3), 4)}
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": steps, "warmup": warm,
@@ -429,7 +453,10 @@ def main():
         "achieved_GBps": round(gbps, 1),
         "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
         "moved_rows_mean": round(float(M.mean()), 1),
+        "copy_peak_GBps": round(copy_gbps, 1),
+        "frac_of_copy_peak": round(gbps / copy_gbps, 4),
         "roofline": roofline,
+        "mfma": mfma,
         "kernels": kernels,
     }
     if not args.no_cpu:

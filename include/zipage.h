@@ -22,8 +22,9 @@
  *   - Device tables are checked by the kernels as they read them: a block id
  *     outside [0, num_blocks), a token count outside its allowed range or a
  *     slot outside [0, num_slots) makes the affected (request, layer, head)
- *     unit skip all memory writes except first_hole[u] = -1 (when that output
- *     is requested) and records ZP_EDEVICE in the workspace.
+ *     unit skip all memory writes except the markers keep_idx[u][0] = -1 and
+ *     first_hole[u] = -1 (when that output is requested), and records
+ *     ZP_EDEVICE in the workspace. zp_update_global leaves such units alone.
  *   - No C++ exception crosses this interface.
  */
 #ifndef ZIPAGE_H

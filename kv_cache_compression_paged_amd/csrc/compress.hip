@@ -190,7 +190,8 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(ScoreArgs a) {
       bad |= dst_tab[j] < 0 || dst_tab[j] >= a.NB;
   }
   if (__syncthreads_or(bad)) {
-    if (tid == 0) {
+    if (tid == 0) {  // markers of a rejected unit; nothing else is written
+      a.keep[static_cast<int64_t>(u) * a.k] = -1;
       if (a.hole_out) a.hole_out[u] = -1;
       *a.err = ZP_EDEVICE;
     }
@@ -633,8 +634,11 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(ScoreArgs a) {
   const int off = zpd::block_exclusive_scan<kWaves>(kept, scratch, &kept_total);
   const int hole = zpd::block_min<kWaves>(first_ev, scratch);
   if (kept_total != a.k) {  // cannot happen for a consistent unit
-    if (tid == 0) *a.err = ZP_EDEVICE;
-    if (tid == 0 && a.hole_out) a.hole_out[u] = -1;
+    if (tid == 0) {
+      a.keep[static_cast<int64_t>(u) * a.k] = -1;
+      if (a.hole_out) a.hole_out[u] = -1;
+      *a.err = ZP_EDEVICE;
+    }
     return;
   }
   // kept positions, ascending: to the output row and (the keys are no longer

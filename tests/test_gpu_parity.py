@@ -126,6 +126,63 @@ def test_prefix_targets_with_block_manager():
            "shared prefix -> target blocks (plans from zp_bm)")
 
 
+def test_device_table_errors_reject_only_their_units():
+    """A block id outside the pool (request 1) and a token count below the
+    trigger (request 2) are caught by the kernel: those units write only
+    their markers (keep row starting with -1, first hole -1), the error word
+    reads ZP_EDEVICE, the global update skips them, and request 0 is
+    compressed as usual."""
+    spec = synth.scaled(EIGHT_B, requests=3)
+    case = P.Case(spec)
+    wl, glob, host, dev, tables, dst, pinned, n_tok, _ = P.build_inputs(case)
+    zparams, oparams = P._params_for(spec, 0)
+    pool = Z.make_pool(wl.k_pool, wl.v_pool)
+    R, L, H, b = spec.requests, spec.layers, spec.kv_heads, spec.block_size
+    U, k, n = R * L * H, spec.keep, spec.n_tokens
+    dev.src_table[1, 5] = spec.pool_blocks + 3
+    dev.n_tokens[2] = spec.n_max * b - 1
+    out = Z.alloc_outputs(U, k, dev.n_cap, "cuda", debug=True)
+    out.keep_idx.fill_(-7)
+    ws = Z.alloc_workspace(pool, zparams, R, "cuda")
+    k_before = wl.k_pool.clone()
+    v_before = wl.v_pool.clone()
+    g_before = glob.clone()
+    Z.zp_compress(pool, dev, wl.q_window, glob, zparams, out, ws)
+    Z.zp_update_global(glob, pool, dev, out, zparams)
+    torch.cuda.synchronize()
+    assert Z.zp_workspace_error(ws) == Z.ZP_EDEVICE
+    assert Z.zp_workspace_error(ws) == Z.ZP_OK  # reading clears the word
+    per_req = L * H
+    bad = slice(per_req, 3 * per_req)
+    assert bool((out.keep_idx[bad, 0] == -1).all())
+    assert bool((out.keep_idx[bad, 1:] == -7).all())
+    assert bool((out.first_hole[bad] == -1).all())
+    assert torch.equal(glob[1:3], g_before[1:3])
+    for r in (1, 2):
+        blocks = torch.from_numpy(tables[r]).cuda().long()
+        assert torch.equal(wl.k_pool[:, blocks], k_before[:, blocks])
+        assert torch.equal(wl.v_pool[:, blocks], v_before[:, blocks])
+    # request 0 against the oracle
+    keep = out.keep_idx.cpu().numpy()
+    for u in range(per_req):
+        l, h = u // H, u % H
+        kr = O.gather_rows(host["k"], tables[0], l, h, n, b)
+        vr = O.gather_rows(host["v"], tables[0], l, h, n, b)
+        q = O.widen(host["q"][0, l, :, h * (spec.q_heads // H):(h + 1) * (spec.q_heads // H)],
+                    spec.dtype)
+        ur = O.score_unit(q, O.widen(kr, spec.dtype), host["g"][0, l, h].astype(np.float64),
+                          n, 0, oparams)
+        diff = set(keep[u].tolist()) ^ set(ur.keep.tolist())
+        fin = np.isfinite(ur.score)
+        tau = min(float(ur.score[t]) for t in ur.keep if fin[t])
+        assert all(abs(ur.score[t] - tau) <= P.BAND for t in diff)
+        blocks = torch.from_numpy(tables[0]).cuda().long()
+        nk = synth.raw_numpy(wl.k_pool[l, blocks, h].reshape(n, -1))
+        nv = synth.raw_numpy(wl.v_pool[l, blocks, h].reshape(n, -1))
+        assert nk[:k].tobytes() == kr[keep[u]].tobytes()
+        assert nv[:k].tobytes() == vr[keep[u]].tobytes()
+
+
 def _forced_global(spec, evict_positions):
     g = np.zeros((spec.requests, spec.layers, spec.kv_heads, spec.n_tokens))
     g[..., list(evict_positions)] = -100.0
@@ -312,10 +369,13 @@ def test_full_size_prefix_sampled():
 
 
 def test_full_size_overlap_sampled():
-    """512 requests in 8 groups: group 0 (64 requests, all 32 layers, holding
-    the query slots) is compressed on one stream while the other 448 requests
-    decode on a second stream. Sampled compressed units and sampled decode
-    (request, layer) pairs are checked against the oracle."""
+    """512 requests in 8 groups. Step 0: group 0 (64 requests, all 32 layers,
+    holding the query slots) is compressed on one stream while the other 448
+    requests decode on a second stream. Step 1: group 1 compresses while group
+    0, now compacted to k tokens, decodes with the rest. Sampled compressed
+    units, sampled decode pairs of step 0, and sampled decode pairs of the
+    compacted group (against the oracle's attention over the kept tokens of
+    the original cache) are checked."""
     spec = synth.OVERLAP
     dev = "cuda"
     per = spec.requests // spec.compress_groups
@@ -352,6 +412,16 @@ def test_full_size_overlap_sampled():
     ready.record(torch.cuda.current_stream())
     sc.wait_event(ready)
     sd.wait_event(ready)
+    # original rows of a few (request, layer) pairs of group 0, for checking
+    # their decode after compaction
+    pairs0 = sorted(set((int(a), int(b)) for a, b in zip(
+        rng.integers(0, per, 16), rng.integers(0, L, 16))))
+    orig0 = {}
+    for (r, l) in pairs0:
+        blocks = tab_c[r].long()
+        orig0[(r, l)] = [(synth.raw_numpy(wl.k_pool[l, blocks, h].reshape(n, -1)),
+                          synth.raw_numpy(wl.v_pool[l, blocks, h].reshape(n, -1)))
+                         for h in range(H)]
     _say(f"[full] compress {Uc} units on stream C, decode {rest.size} requests on stream D")
     Z.zp_compress(pool, batch, wl.q_window, wl.global_scores, zparams, out, ws, sc)
     Z.zp_update_global(wl.global_scores, pool, batch, out, zparams, sc)
@@ -379,5 +449,48 @@ def test_full_size_overlap_sampled():
             err = np.abs(got[i, l, h * G:(h + 1) * G] - want)
             assert np.all(err <= 1e-4 * np.abs(want) + 1e-5), (r, l, h, err.max())
     _say(f"[full] {spec.name}: {len(pairs)} sampled decode pairs match")
-    del wl, out, dec
+
+    # step 1: group 1 compresses; group 0 decodes its k kept tokens
+    keep0 = out.keep_idx.cpu().numpy()
+    grp1 = np.arange(per, 2 * per)
+    dec_reqs = np.concatenate([grp, np.arange(2 * per, spec.requests)])
+    lens1 = np.concatenate([np.full(per, k, dtype=np.int32),
+                            rng.integers(k + 1, n, size=dec_reqs.size - per).astype(np.int32)])
+    tab_c1 = torch.from_numpy(np.ascontiguousarray(tables[grp1])).to(dev)
+    tab_d1 = torch.from_numpy(np.ascontiguousarray(tables[dec_reqs])).to(dev)
+    batch1 = Z.DeviceBatch(
+        slot=torch.arange(per, dtype=torch.int32, device=dev),
+        n_tokens=torch.full((per,), n, dtype=torch.int32, device=dev),
+        src_table=tab_c1, dst_table=tab_c1.clone(),
+        n_pinned=torch.zeros(per, dtype=torch.int32, device=dev),
+        num_slots=per, n_cap=wl.n_cap)
+    q1 = synth.decode_queries(spec, dec_reqs.size, dev, spec.seed + 5)
+    dec1 = torch.full((dec_reqs.size, L, spec.q_heads, spec.head_dim), float("nan"),
+                      dtype=torch.float32, device=dev)
+    lens1_dev = torch.from_numpy(lens1).to(dev)
+    ready.record(torch.cuda.current_stream())
+    sc.wait_event(ready)
+    sd.wait_event(ready)
+    _say(f"[full] step 1: compress group 1, decode {dec_reqs.size} requests "
+         f"(group 0 at k = {k})")
+    Z.zp_compress(pool, batch1, wl.q_window, wl.global_scores, zparams, out, ws, sc)
+    Z.zp_update_global(wl.global_scores, pool, batch1, out, zparams, sc)
+    Z.zp_paged_decode(dec1, q1, pool, tab_d1, lens1_dev, zparams, sd)
+    torch.cuda.synchronize()
+    assert Z.zp_workspace_error(ws) == Z.ZP_OK
+    _check_all_units(spec, out, wl.global_scores, False)
+    q1h = synth.raw_numpy(q1)
+    got1 = dec1.cpu().numpy().astype(np.float64)
+    for (r, l) in pairs0:  # group 0 comes first in dec_reqs
+        for h in range(H):
+            u = (r * L + l) * H + h
+            kr, vr = orig0[(r, l)][h]
+            kk = keep0[u]
+            want = O.decode_attention(O.widen(q1h[r, l, h * G:(h + 1) * G], spec.dtype),
+                                      O.widen(kr[kk], spec.dtype), O.widen(vr[kk], spec.dtype))
+            err = np.abs(got1[r, l, h * G:(h + 1) * G] - want)
+            assert np.all(err <= 1e-4 * np.abs(want) + 1e-5), (r, l, h, err.max())
+    _say(f"[full] {spec.name}: {len(pairs0)} decode pairs of the compacted group "
+         f"match the oracle over their kept tokens")
+    del wl, out, dec, dec1
     torch.cuda.empty_cache()
