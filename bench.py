@@ -20,6 +20,9 @@ compressed on stream C while the other 448 requests decode one token over all
 32 layers on stream D. Each step times C alone, D alone and both together;
 the line reports compressed tokens/s under overlap plus the three times.
 
+With --workload capture_8b_32L_32q it times query-window capture alone (128
+slot-holding requests x 32 layers x 32 query heads of 128, w = 32).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        [--cpu-seconds S] [--no-cpu]
 """
@@ -304,6 +307,52 @@ def run_overlap(args, spec):
     print(json.dumps(result), flush=True)
 
 
+def run_capture(args):
+    """Query-window capture at the 8B-like shape: 128 slot-holding requests,
+    32 layers, 32 query heads of 128 (bf16), w = 32. One call moves each
+    request's new-token queries of all layers into its ring rows."""
+    import torch
+    import kv_cache_compression_paged_amd as Z
+    dev = "cuda"
+    R, L, Hq, d, w = 128, 32, 32, 128, 32
+    ring = torch.zeros((R, L, w, Hq, d), dtype=torch.bfloat16, device=dev)
+    q = torch.randn((R, L, Hq, d), device=dev).to(torch.bfloat16)
+    slot = torch.arange(R, dtype=torch.int32, device=dev)
+    params = Z.make_params(256, w, Hq, Z.ZP_BF16)
+    calls = max(args.steps, 1) * 20
+    poss = [torch.full((R,), 4000 + i, dtype=torch.int32, device=dev)
+            for i in range(calls + args.warmup)]
+    for i in range(args.warmup):
+        Z.zp_capture_queries(ring, q, slot, poss[i], params)
+    torch.cuda.synchronize()
+    Z.timing_read()
+    Z.timing_enable(True)
+    t0 = time.perf_counter()
+    for i in range(calls):
+        Z.zp_capture_queries(ring, q, slot, poss[args.warmup + i], params)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    Z.timing_enable(False)
+    cnt, tot = Z.timing_read()["capture"]
+    avg_ms = tot / cnt
+    nbytes = 2.0 * R * L * Hq * d * 2
+    ach = nbytes / (avg_ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "query rows captured/sec (query-window capture)",
+        "value": round(R * L / (avg_ms * 1e-3), 1), "unit": "rows/s",
+        "n_gpus": 1, "steps": calls, "warmup": args.warmup,
+        "ms_per_step": round(avg_ms, 5), "wall_ms_per_call": round(elapsed * 1e3 / calls, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "capture_8b_32L_32q", "requests": R, "layers": L,
+                   "q_heads": Hq, "head_dim": d, "window": w},
+        "roofline": {"bound": "hbm", "kernel": "capture", "achieved": round(ach, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "alg_bytes_per_launch": round(nbytes)},
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -318,6 +367,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     Z.lib()
+    if args.workload == "capture_8b_32L_32q":
+        run_capture(args)
+        return
     spec = synth.SPECS[args.workload]
     if spec.compress_groups > 1:
         run_overlap(args, spec)

@@ -54,6 +54,9 @@ typedef int32_t zp_status;
 /* zp_params.flags */
 #define ZP_NONCAUSAL      (1u << 0) /* window rows see all n tokens           */
 #define ZP_PROTECT_WINDOW (1u << 1) /* the last w tokens are always kept      */
+#define ZP_WINDOW_RING    (1u << 2) /* q_window rows form a ring: the query of
+                                       position p sits in row p mod w (the
+                                       layout zp_capture_queries writes)     */
 
 /* A paged KV pool: k and v are device arrays laid out
  * [layers][num_blocks][kv_heads][block_size][head_dim] of `dtype`, 16-byte
@@ -84,7 +87,7 @@ typedef struct {
  *               - w_red*red (the pages name the three parts, [zh] §2.1,
  *               without a formula; 1, 0.5, 0.5 is the documented default).
  *   sm_scale -- softmax scale; <= 0 selects 1/sqrt(head_dim).
- *   flags    -- ZP_NONCAUSAL, ZP_PROTECT_WINDOW. */
+ *   flags    -- ZP_NONCAUSAL, ZP_PROTECT_WINDOW, ZP_WINDOW_RING. */
 typedef struct {
   int32_t  n_max;
   int32_t  window;
@@ -204,6 +207,26 @@ zp_status zp_paged_decode(float* out, const void* q, const zp_kv_pool* pool,
                           const int32_t* seq_lens, int32_t num_reqs,
                           const zp_params* params, void* stream);
 
+/* Query-window capture, the step before compression ([zh] §2.2, [de] §2: only
+ * requests that hold a query slot keep their recent queries; [zh] §2.1: the
+ * last w queries score the cache). For every request r with a slot
+ * (0 <= slot[r] < num_slots) and pos[r] >= 0, the post-RoPE queries of its
+ * new token at position pos[r] are written for every layer l to
+ *   q_window[slot[r]][l][pos[r] mod w][:][:]
+ * so the window of a slot is a ring over the last w positions; zp_compress
+ * reads it with ZP_WINDOW_RING. Requests without a slot (slot[r] < 0, the
+ * slot-free decoding of [zh] §2.2) and any with a slot or position out of
+ * range are skipped.
+ * q_window: device [num_slots][layers][w][q_heads][head_dim]; q: device
+ * [num_reqs][layers][q_heads][head_dim]; both of params->q_dtype, 16-byte
+ * aligned. slot, pos: device [num_reqs] int32. Only params->window, q_heads
+ * and q_dtype are read. Errors: ZP_EINVAL, ZP_EUNSUPPORTED (head_dim not
+ * 64/128), ZP_EHIP. */
+zp_status zp_capture_queries(void* q_window, const void* q, const int32_t* slot,
+                             const int32_t* pos, int32_t num_reqs, int32_t layers,
+                             int32_t num_slots, int32_t head_dim,
+                             const zp_params* params, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Host-side block bookkeeping (no GPU calls). A block manager owns the free
  * list and the reference counts of a pool of num_blocks blocks. The free list
@@ -271,7 +294,8 @@ int32_t zp_plan_targets(const zp_plan* plan, int32_t* ids, int32_t cap);
 #define ZP_KERNEL_COMPRESS 0  /* score, select and K/V compaction            */
 #define ZP_KERNEL_GLOBAL   1  /* global-score update                         */
 #define ZP_KERNEL_DECODE   2  /* paged decode                                */
-#define ZP_KERNEL_KINDS    3
+#define ZP_KERNEL_CAPTURE  3  /* query-window capture                        */
+#define ZP_KERNEL_KINDS    4
 
 zp_status zp_timing_enable(int32_t enable);
 zp_status zp_timing_read(int32_t* launches /*[ZP_KERNEL_KINDS]*/,

@@ -35,16 +35,19 @@ ZP_BF16 = 1
 
 ZP_NONCAUSAL = 1 << 0
 ZP_PROTECT_WINDOW = 1 << 1
+ZP_WINDOW_RING = 1 << 2
 
 ZP_KERNEL_COMPRESS = 0
 ZP_KERNEL_GLOBAL = 1
 ZP_KERNEL_DECODE = 2
-ZP_KERNEL_KINDS = 3
-KERNEL_NAMES = ("compress", "global_update", "paged_decode")
+ZP_KERNEL_CAPTURE = 3
+ZP_KERNEL_KINDS = 4
+KERNEL_NAMES = ("compress", "global_update", "paged_decode", "capture")
 
 EXPORTED = (
     "zp_compress_workspace_bytes", "zp_compress", "zp_update_global",
-    "zp_workspace_error", "zp_paged_decode", "zp_bm_create", "zp_bm_destroy",
+    "zp_workspace_error", "zp_paged_decode", "zp_capture_queries",
+    "zp_bm_create", "zp_bm_destroy",
     "zp_bm_alloc", "zp_bm_incref", "zp_bm_release", "zp_bm_free_count",
     "zp_bm_refcount", "zp_bm_free_list", "zp_bm_plan_compress",
     "zp_bm_commit", "zp_bm_abort", "zp_plan_freed", "zp_plan_targets",
@@ -115,6 +118,7 @@ def lib() -> ctypes.CDLL:
         "zp_update_global": (I32, [P, P, P, P, P, P]),
         "zp_workspace_error": (I32, [P, P, P]),
         "zp_paged_decode": (I32, [P, P, P, P, I32, P, I32, P, P]),
+        "zp_capture_queries": (I32, [P, P, P, P, I32, I32, I32, I32, P, P]),
         "zp_bm_create": (P, [I32]),
         "zp_bm_destroy": (None, [P]),
         "zp_bm_alloc": (I32, [P, I32, P]),
@@ -289,6 +293,17 @@ def zp_paged_decode(out, q, pool: KVPool, block_tables, seq_lens,
            "zp_paged_decode")
 
 
+def zp_capture_queries(q_window, q, slot, pos, params: Params,
+                       stream=None) -> None:
+    """q_window [slots][L][w][Hq][d], q [R][L][Hq][d] (same dtype), slot and
+    pos [R] int32 device tensors."""
+    S, L = q_window.shape[0], q_window.shape[1]
+    R = q.shape[0]
+    _check(lib().zp_capture_queries(_ptr(q_window), _ptr(q), _ptr(slot), _ptr(pos),
+                                    R, L, S, q.shape[-1], ctypes.byref(params),
+                                    _stream_handle(stream)), "zp_capture_queries")
+
+
 def timing_enable(on: bool) -> None:
     _check(lib().zp_timing_enable(1 if on else 0), "zp_timing_enable")
 
@@ -403,6 +418,7 @@ __all__: Tuple[str, ...] = (
     "make_pool", "make_params", "DeviceBatch", "Outputs", "alloc_outputs",
     "alloc_workspace", "zp_compress_workspace_bytes", "zp_compress",
     "zp_update_global", "zp_workspace_error", "zp_paged_decode",
+    "zp_capture_queries",
     "timing_enable", "timing_read", "BlockManager", "Plan", "version",
     "EXPORTED",
 )

@@ -123,7 +123,7 @@ zp_status make_geom(const zp_kv_pool* pool, const zp_params* p,
   if (!std::isfinite(p->w_attn) || !std::isfinite(p->w_global) ||
       !std::isfinite(p->w_red) || !std::isfinite(p->sm_scale))
     return fail(ZP_EINVAL, "score weights and scale must be finite");
-  if (p->flags & ~(ZP_NONCAUSAL | ZP_PROTECT_WINDOW))
+  if (p->flags & ~(ZP_NONCAUSAL | ZP_PROTECT_WINDOW | ZP_WINDOW_RING))
     return fail(ZP_EINVAL, "unknown flags 0x%x", p->flags);
   const int k = (p->n_max - 1) * pool->block_size;
   if ((p->flags & ZP_PROTECT_WINDOW) && p->window > k)
@@ -284,6 +284,34 @@ zp_status zp_paged_decode(float* out, const void* q, const zp_kv_pool* pool,
   timing_before(ZP_KERNEL_DECODE, stream);
   st = launch_decode(g, out, q, *pool, block_tables, seq_lens, stream);
   timing_after(ZP_KERNEL_DECODE, stream);
+  return st;
+}
+
+zp_status zp_capture_queries(void* q_window, const void* q, const int32_t* slot,
+                             const int32_t* pos, int32_t num_reqs, int32_t layers,
+                             int32_t num_slots, int32_t head_dim,
+                             const zp_params* params, void* stream) {
+  if (!params || num_reqs < 0 || layers < 1 || num_slots < 1)
+    return fail(ZP_EINVAL, "zp_capture_queries: bad arguments");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(ZP_EUNSUPPORTED, "zp_capture_queries: head_dim %d", head_dim);
+  if (params->q_dtype != ZP_F32 && params->q_dtype != ZP_BF16)
+    return fail(ZP_EINVAL, "zp_capture_queries: q_dtype %d", params->q_dtype);
+  if (params->window < 1 || params->q_heads < 1)
+    return fail(ZP_EINVAL, "zp_capture_queries: window and q_heads must be >= 1");
+  if (num_reqs == 0) return ZP_OK;
+  if (!q_window || !q || !slot || !pos)
+    return fail(ZP_EINVAL, "zp_capture_queries: NULL device array");
+  if (!aligned16(q_window) || !aligned16(q))
+    return fail(ZP_EINVAL, "zp_capture_queries: q_window and q must be 16-byte aligned");
+  const int64_t rows = static_cast<int64_t>(num_reqs) * layers;
+  if (rows > (1ll << 31) - 1) return fail(ZP_EINVAL, "zp_capture_queries: too many rows");
+  const int32_t row_bytes =
+      params->q_heads * head_dim * (params->q_dtype == ZP_BF16 ? 2 : 4);
+  timing_before(ZP_KERNEL_CAPTURE, stream);
+  const zp_status st = launch_capture(q_window, q, slot, pos, num_reqs, layers,
+                                      num_slots, params->window, row_bytes, stream);
+  timing_after(ZP_KERNEL_CAPTURE, stream);
   return st;
 }
 

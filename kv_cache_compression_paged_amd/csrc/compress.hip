@@ -211,7 +211,10 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(ScoreArgs a) {
     for (int rt = 0; rt < RTW; ++rt) {
       const int row = (rt0 + rt) * 16 + nl;
       if (rt < nrt && row < a.wG) {
-        const int i = row / a.G, g = row - i * a.G;
+        // window row i holds position n - w + i, or, in a ring, row
+        // (n - w + i) mod w does
+        const int i0 = row / a.G, g = row - i0 * a.G;
+        const int i = (a.flags & ZP_WINDOW_RING) ? (n - a.w + i0) % a.w : i0;
         q[rt].load(qbase + (static_cast<int64_t>(i) * a.Hq + h * a.G + g) * D * E::kBytes +
                    jg * (D / 4) * E::kBytes);
       } else {

@@ -34,6 +34,11 @@ zp_status launch_global(const CompressGeom& g, float* global_scores,
                         const zp_batch& batch, const int32_t* keep,
                         const float* attn, void* stream);
 
+zp_status launch_capture(void* q_window, const void* q, const int32_t* slot,
+                         const int32_t* pos, int32_t num_reqs, int32_t layers,
+                         int32_t num_slots, int32_t window, int32_t row_bytes,
+                         void* stream);
+
 struct DecodeGeom {
   int32_t R, L, Hkv, Hq, G, d, b, num_blocks, max_blocks, dtype, q_dtype;
   float scale_log2;

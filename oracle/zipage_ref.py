@@ -143,6 +143,29 @@ def window_positions(n: int, w: int) -> List[int]:
     return [n - w + i for i in range(w)]
 
 
+def capture_queries(q_window: np.ndarray, q: np.ndarray, slot: Sequence[int],
+                    pos: Sequence[int], w: int) -> None:
+    """Query slots ([zh] §2.2, [de] §2): only requests holding a slot keep
+    their recent query states, and the last w of them score the cache
+    ([zh] §2.1). Reading: each slot keeps, per layer, a ring of w rows; the
+    queries (all query heads) of the token at position p go to row p mod w.
+    q_window: raw [slots][L][w][Hq][d], updated in place; q: raw
+    [R][L][Hq][d]. A request with slot < 0 (no slot), a slot out of range or
+    a negative position writes nothing."""
+    S = q_window.shape[0]
+    for r in range(q.shape[0]):
+        s, p = int(slot[r]), int(pos[r])
+        if s < 0 or s >= S or p < 0:
+            continue
+        for layer in range(q.shape[1]):
+            q_window[s, layer, p % w] = q[r, layer]
+
+
+def window_from_ring(ring: np.ndarray, n: int, w: int) -> np.ndarray:
+    """The w rows of one (slot, layer) ring in position order n-w .. n-1."""
+    return np.stack([ring[(n - w + i) % w] for i in range(w)])
+
+
 def window_attention(q_win: np.ndarray, keys: np.ndarray, n: int,
                      causal: bool = True,
                      sm_scale: Optional[float] = None) -> np.ndarray:

@@ -219,3 +219,29 @@ def test_decode_rejects_bad_arguments():
     r = lib.zp_paged_decode(FAKE, FAKE, ctypes.byref(_pool()), FAKE, 4, FAKE, 0,
                             ctypes.byref(_params()), None)
     assert r == Z.ZP_OK
+
+
+def test_capture_rejects_bad_arguments():
+    lib = Z.lib()
+    P = ctypes.byref
+
+    def cap(q_window=FAKE, q=FAKE, slot=FAKE, pos=FAKE, R=2, L=2, S=4, d=128,
+            params=None):
+        return lib.zp_capture_queries(q_window, q, slot, pos, R, L, S, d,
+                                      P(params or _params()), None)
+    assert cap(d=80) == Z.ZP_EUNSUPPORTED
+    assert cap(L=0) == Z.ZP_EINVAL
+    assert cap(S=0) == Z.ZP_EINVAL
+    assert cap(R=-1) == Z.ZP_EINVAL
+    assert cap(params=_params(window=0)) == Z.ZP_EINVAL
+    assert cap(params=_params(q_dtype=7)) == Z.ZP_EINVAL
+    assert cap(slot=None) == Z.ZP_EINVAL
+    assert cap(q=FAKE + 4) == Z.ZP_EINVAL           # misaligned
+    assert cap(R=0, q=None, slot=None) == Z.ZP_OK   # empty batch: nothing to do
+
+
+def test_window_ring_flag_is_accepted_by_validation():
+    # an unknown flag bit is rejected; ZP_WINDOW_RING is known
+    b = _batch(num_reqs=0)
+    assert _compress(params=_params(flags=Z.ZP_WINDOW_RING), batch=b) == Z.ZP_OK
+    assert _compress(params=_params(flags=1 << 7), batch=b) == Z.ZP_EINVAL

@@ -129,3 +129,29 @@ def test_planted_mistake_is_caught(name, mutant, pin, args):
     assert not _fails(pin, *args), "pin must pass on the real oracle"
     with planted(name, mutant):
         assert _fails(pin, *args), f"{mutant.__name__} slipped past {pin.__name__}"
+
+
+def capture_row_off_by_one(q_window, q, slot, pos, w):
+    S = q_window.shape[0]
+    for r in range(q.shape[0]):
+        s, p = int(slot[r]), int(pos[r])
+        if s < 0 or s >= S or p < 0:
+            continue
+        for layer in range(q.shape[1]):
+            q_window[s, layer, (p + 1) % w] = q[r, layer]   # should be p % w
+
+
+def capture_ignores_slot(q_window, q, slot, pos, w):
+    for r in range(q.shape[0]):
+        p = int(pos[r])
+        s = max(int(slot[r]), 0) % q_window.shape[0]          # no skip
+        for layer in range(q.shape[1]):
+            q_window[s, layer, p % w] = q[r, layer]
+
+
+@pytest.mark.parametrize("fn", [capture_row_off_by_one, capture_ignores_slot])
+def test_capture_mistakes_are_caught(fn):
+    with planted("capture_queries", fn):
+        caught = (_fails(P.test_capture_ring_holds_the_last_w_queries, 4, 11)
+                  or _fails(P.test_capture_skips_requests_without_a_slot))
+    assert caught

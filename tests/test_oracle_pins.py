@@ -426,3 +426,54 @@ def test_decode_attention_equals_torch_sdpa():
         torch.from_numpy(q)[None], torch.from_numpy(keys)[None],
         torch.from_numpy(vals)[None])[0].numpy()
     np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# query-window capture ([zh] §2.2 query slots; [zh] §2.1 last w queries)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("w,P", [(1, 5), (4, 4), (4, 11), (8, 37), (32, 100)])
+def test_capture_ring_holds_the_last_w_queries(w, P):
+    """Capturing positions 0..P-1 one decode step at a time leaves, read in
+    position order, exactly the queries of the last w positions (a plain
+    slice of the sequence)."""
+    rng = np.random.default_rng(w * 1000 + P)
+    L, Hq, d = 2, 3, 4
+    seq = rng.standard_normal((P, L, Hq, d))      # queries of positions 0..P-1
+    ring = np.zeros((2, L, w, Hq, d))
+    for p in range(P):
+        O.capture_queries(ring, seq[p][None], [1], [p], w)
+    for layer in range(L):
+        got = O.window_from_ring(ring[1, layer], P, w)
+        assert np.array_equal(got, seq[P - w:P, layer])
+    assert not ring[0].any()                       # the other slot untouched
+
+
+def test_capture_skips_requests_without_a_slot():
+    rng = np.random.default_rng(3)
+    w, L, Hq, d = 4, 1, 2, 4
+    ring = np.full((2, L, w, Hq, d), 7.0)
+    q = rng.standard_normal((4, L, Hq, d))
+    O.capture_queries(ring, q, [-1, 2, 0, 1], [5, 6, -1, 9], w)
+    # request 0: no slot; 1: slot 2 out of range; 2: negative position
+    assert np.array_equal(ring[0], np.full((L, w, Hq, d), 7.0))
+    expect = np.full((L, w, Hq, d), 7.0)
+    expect[:, 9 % w] = q[3]
+    assert np.array_equal(ring[1], expect)
+
+
+def test_ring_window_scores_like_the_linear_window():
+    """A compression that reads its window through the ring gives the same
+    attention as one handed the last w queries in order (closed ring walk
+    against a direct slice)."""
+    rng = np.random.default_rng(11)
+    n, w, G, d = 40, 6, 2, 8
+    keys = rng.standard_normal((n, d))
+    seq = rng.standard_normal((n, 1, G, d))
+    ring = np.zeros((1, 1, w, G, d))
+    for p in range(n):
+        O.capture_queries(ring, seq[p][None], [0], [p], w)
+    lin = seq[n - w:, 0]
+    a1 = O.window_attention(lin, keys, n, True)
+    a2 = O.window_attention(O.window_from_ring(ring[0, 0], n, w), keys, n, True)
+    assert np.array_equal(a1, a2)
