@@ -21,7 +21,9 @@ compressed on stream C while the other 448 requests decode one token over all
 the line reports compressed tokens/s under overlap plus the three times.
 
 With --workload capture_8b_32L_32q it times query-window capture alone (128
-slot-holding requests x 32 layers x 32 query heads of 128, w = 32).
+slot-holding requests x 32 layers x 32 query heads of 128, w = 32); with
+--workload decode_8b_32L_8kv_32q the decode consumer (plain, with append, and
+split-K on a long-context small batch).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        [--cpu-seconds S] [--no-cpu]
@@ -353,6 +355,85 @@ def run_capture(args):
     }), flush=True)
 
 
+def run_decode(args):
+    """Decode consumer on the 8B-like pool: (a) 128 requests x 32 layers at the
+    compressed length k = 4080, plain and with the new token appended; (b) a
+    long-context, small batch (4 requests of 16384 tokens) with one wave per
+    unit against split-K."""
+    import torch
+    import kv_cache_compression_paged_amd as Z
+    from kv_cache_compression_paged_amd import synth
+    spec = synth.EIGHT_B
+    dev = "cuda"
+    wl = synth.make(spec, device=dev)
+    R, L, H, d = spec.requests, spec.layers, spec.kv_heads, spec.head_dim
+    params = Z.make_params(spec.n_max, spec.window, spec.q_heads, Z.ZP_BF16)
+    pool = Z.make_pool(wl.k_pool, wl.v_pool)
+    reps = max(args.steps, 1)
+
+    def timed(fn):
+        for _ in range(max(args.warmup, 1)):
+            fn()
+        torch.cuda.synchronize()
+        Z.timing_read()
+        Z.timing_enable(True)
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        Z.timing_enable(False)
+        cnt, tot = Z.timing_read()["paged_decode"]
+        return tot / cnt
+
+    def kv_bytes(lens, reqs):
+        return 2.0 * 2 * d * float(np.sum(lens)) * L * H + reqs * L * spec.q_heads * d * (2 + 4)
+
+    res = {}
+    tab = torch.from_numpy(wl.tables).to(dev)
+    lens = np.full(R, spec.keep, dtype=np.int32)
+    lens_dev = torch.from_numpy(lens).to(dev)
+    q = synth.decode_queries(spec, R, dev, spec.seed + 7)
+    out = torch.empty((R, L, spec.q_heads, d), dtype=torch.float32, device=dev)
+    k_new = torch.randn((R, L, H, d), device=dev).to(torch.bfloat16)
+    v_new = torch.randn((R, L, H, d), device=dev).to(torch.bfloat16)
+    b_plain = kv_bytes(lens, R)
+    t = timed(lambda: Z.zp_paged_decode(out, q, pool, tab, lens_dev, params))
+    res["plain_128req_len4080"] = {"ms": round(t, 4), "GBps": round(b_plain / (t * 1e-3) / 1e9, 1)}
+    b_app = kv_bytes(lens + 1, R) + 2.0 * R * L * H * d * 2
+    t = timed(lambda: Z.zp_paged_decode_append(out, q, k_new, v_new, pool, tab, lens_dev,
+                                               params))
+    res["append_128req_len4080"] = {"ms": round(t, 4), "GBps": round(b_app / (t * 1e-3) / 1e9, 1)}
+    # long context: 4 requests of 1024 blocks each, tables from the same pool
+    RL, nb = 4, 1024
+    tl = torch.from_numpy(np.ascontiguousarray(
+        wl.tables.reshape(-1)[:RL * nb].reshape(RL, nb))).to(dev)
+    ll = np.full(RL, nb * 16, dtype=np.int32)
+    ll_dev = torch.from_numpy(ll).to(dev)
+    ql = synth.decode_queries(spec, RL, dev, spec.seed + 8)
+    ol = torch.empty((RL, L, spec.q_heads, d), dtype=torch.float32, device=dev)
+    b_long = kv_bytes(ll, RL)
+    for splits in (1, 4, 16, 64):
+        nbytes = Z.zp_decode_workspace_bytes(pool, params, RL, splits)
+        ws = torch.empty(max(nbytes, 256) // 4 + 64, dtype=torch.int32, device=dev)
+        t = timed(lambda: Z.zp_paged_decode_split(ol, ql, pool, tl, ll_dev, params, splits,
+                                                  ws if splits > 1 else None))
+        res[f"long_4req_len16384_splits{splits}"] = {
+            "ms": round(t, 4), "GBps": round(b_long / (t * 1e-3) / 1e9, 1)}
+    best = res["plain_128req_len4080"]
+    print(json.dumps({
+        "metric": "paged decode KV GB/s (consumer of the compressed cache)",
+        "value": best["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": reps,
+        "warmup": args.warmup, "ms_per_step": best["ms"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "decode_8b_32L_8kv_32q", "layers": L, "kv_heads": H,
+                   "q_heads": spec.q_heads, "head_dim": d},
+        "roofline": {"bound": "hbm", "kernel": "paged_decode", "achieved": best["GBps"],
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(best["GBps"] / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "alg_bytes_per_launch": round(b_plain)},
+        "cases": res,
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -369,6 +450,9 @@ def main():
     Z.lib()
     if args.workload == "capture_8b_32L_32q":
         run_capture(args)
+        return
+    if args.workload == "decode_8b_32L_8kv_32q":
+        run_decode(args)
         return
     spec = synth.SPECS[args.workload]
     if spec.compress_groups > 1:

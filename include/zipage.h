@@ -207,6 +207,38 @@ zp_status zp_paged_decode(float* out, const void* q, const zp_kv_pool* pool,
                           const int32_t* seq_lens, int32_t num_reqs,
                           const zp_params* params, void* stream);
 
+/* Decode step with the new token appended ([zh] §2.3: decoding appends to the
+ * request's tail block): for every (r, l, kv head h) the new token's rows
+ * k_new[r][l][h][:] and v_new[r][l][h][:] are written to position seq_lens[r]
+ * (block block_tables[r][seq_lens[r] / b], slot seq_lens[r] mod b) and out is
+ * the attention of q over the seq_lens[r] + 1 tokens, the new one included.
+ * seq_lens[r] counts the tokens cached before the call (0 allowed) and is not
+ * changed; ceil((seq_lens[r] + 1) / b) <= max_blocks. k_new, v_new: device
+ * [num_reqs][layers][kv_heads][head_dim] of the pool dtype, 16-byte aligned.
+ * A unit with a bad length or block id writes nothing (neither the slot nor
+ * out). Errors: as zp_paged_decode. */
+zp_status zp_paged_decode_append(float* out, const void* q, const void* k_new,
+                                 const void* v_new, const zp_kv_pool* pool,
+                                 const int32_t* block_tables, int32_t max_blocks,
+                                 const int32_t* seq_lens, int32_t num_reqs,
+                                 const zp_params* params, void* stream);
+
+/* Split-K decode for long contexts with few units: each (request, layer, kv
+ * head) is spread over `splits` waves (1..256), each taking a contiguous range
+ * of the unit's blocks; a second kernel merges their partial (max, sum, P.V)
+ * with the usual softmax rescaling. k_new / v_new: NULL, or an append as in
+ * zp_paged_decode_append. workspace: device, 256-byte aligned, at least
+ * zp_decode_workspace_bytes(pool, params, num_reqs, splits) bytes (0 for
+ * splits == 1). Errors: as zp_paged_decode, plus ZP_EWORKSPACE. */
+zp_status zp_decode_workspace_bytes(const zp_kv_pool* pool, const zp_params* params,
+                                    int32_t num_reqs, int32_t splits, size_t* bytes);
+zp_status zp_paged_decode_split(float* out, const void* q, const void* k_new,
+                                const void* v_new, const zp_kv_pool* pool,
+                                const int32_t* block_tables, int32_t max_blocks,
+                                const int32_t* seq_lens, int32_t num_reqs,
+                                const zp_params* params, int32_t splits, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 /* Query-window capture, the step before compression ([zh] §2.2, [de] §2: only
  * requests that hold a query slot keep their recent queries; [zh] §2.1: the
  * last w queries score the cache). For every request r with a slot

@@ -46,7 +46,8 @@ KERNEL_NAMES = ("compress", "global_update", "paged_decode", "capture")
 
 EXPORTED = (
     "zp_compress_workspace_bytes", "zp_compress", "zp_update_global",
-    "zp_workspace_error", "zp_paged_decode", "zp_capture_queries",
+    "zp_workspace_error", "zp_paged_decode", "zp_paged_decode_append",
+    "zp_decode_workspace_bytes", "zp_paged_decode_split", "zp_capture_queries",
     "zp_bm_create", "zp_bm_destroy",
     "zp_bm_alloc", "zp_bm_incref", "zp_bm_release", "zp_bm_free_count",
     "zp_bm_refcount", "zp_bm_free_list", "zp_bm_plan_compress",
@@ -119,6 +120,9 @@ def lib() -> ctypes.CDLL:
         "zp_workspace_error": (I32, [P, P, P]),
         "zp_paged_decode": (I32, [P, P, P, P, I32, P, I32, P, P]),
         "zp_capture_queries": (I32, [P, P, P, P, I32, I32, I32, I32, P, P]),
+        "zp_paged_decode_append": (I32, [P, P, P, P, P, P, I32, P, I32, P, P]),
+        "zp_decode_workspace_bytes": (I32, [P, P, I32, I32, P]),
+        "zp_paged_decode_split": (I32, [P, P, P, P, P, P, I32, P, I32, P, I32, P, U, P]),
         "zp_bm_create": (P, [I32]),
         "zp_bm_destroy": (None, [P]),
         "zp_bm_alloc": (I32, [P, I32, P]),
@@ -293,6 +297,36 @@ def zp_paged_decode(out, q, pool: KVPool, block_tables, seq_lens,
            "zp_paged_decode")
 
 
+def zp_paged_decode_append(out, q, k_new, v_new, pool: KVPool, block_tables,
+                           seq_lens, params: Params, stream=None) -> None:
+    R, mb = block_tables.shape
+    _check(lib().zp_paged_decode_append(_ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                        ctypes.byref(pool), _ptr(block_tables), mb,
+                                        _ptr(seq_lens), R, ctypes.byref(params),
+                                        _stream_handle(stream)), "zp_paged_decode_append")
+
+
+def zp_decode_workspace_bytes(pool: KVPool, params: Params, num_reqs: int,
+                              splits: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().zp_decode_workspace_bytes(ctypes.byref(pool), ctypes.byref(params),
+                                           num_reqs, splits, ctypes.byref(out)),
+           "zp_decode_workspace_bytes")
+    return out.value
+
+
+def zp_paged_decode_split(out, q, pool: KVPool, block_tables, seq_lens,
+                          params: Params, splits: int, workspace, k_new=None,
+                          v_new=None, stream=None) -> None:
+    R, mb = block_tables.shape
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().zp_paged_decode_split(_ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                       ctypes.byref(pool), _ptr(block_tables), mb,
+                                       _ptr(seq_lens), R, ctypes.byref(params), splits,
+                                       _ptr(workspace), nbytes, _stream_handle(stream)),
+           "zp_paged_decode_split")
+
+
 def zp_capture_queries(q_window, q, slot, pos, params: Params,
                        stream=None) -> None:
     """q_window [slots][L][w][Hq][d], q [R][L][Hq][d] (same dtype), slot and
@@ -418,7 +452,8 @@ __all__: Tuple[str, ...] = (
     "make_pool", "make_params", "DeviceBatch", "Outputs", "alloc_outputs",
     "alloc_workspace", "zp_compress_workspace_bytes", "zp_compress",
     "zp_update_global", "zp_workspace_error", "zp_paged_decode",
-    "zp_capture_queries",
+    "zp_capture_queries", "zp_paged_decode_append", "zp_decode_workspace_bytes",
+    "zp_paged_decode_split",
     "timing_enable", "timing_read", "BlockManager", "Plan", "version",
     "EXPORTED",
 )

@@ -249,24 +249,51 @@ zp_status zp_workspace_error(void* workspace, void* stream, int32_t* code) {
   return ZP_OK;
 }
 
-zp_status zp_paged_decode(float* out, const void* q, const zp_kv_pool* pool,
-                          const int32_t* block_tables, int32_t max_blocks,
-                          const int32_t* seq_lens, int32_t num_reqs,
-                          const zp_params* params, void* stream) {
+namespace {
+
+constexpr int kMaxSplits = 256;
+
+size_t decode_ws_bytes(const zp_kv_pool* pool, const zp_params* params, int32_t num_reqs,
+                       int32_t splits) {
+  return static_cast<size_t>(num_reqs) * pool->layers * params->q_heads * splits *
+         (pool->head_dim + 2) * sizeof(float);
+}
+
+// Shared checks and launch of the three decode entry points.
+zp_status decode_common(const char* name, float* out, const void* q, const void* k_new,
+                        const void* v_new, const zp_kv_pool* pool,
+                        const int32_t* block_tables, int32_t max_blocks,
+                        const int32_t* seq_lens, int32_t num_reqs,
+                        const zp_params* params, int32_t splits, void* workspace,
+                        size_t workspace_bytes, void* stream) {
   zp_status st = check_pool(pool);
   if (st != ZP_OK) return st;
   if (!params || num_reqs < 0 || max_blocks < 1)
-    return fail(ZP_EINVAL, "zp_paged_decode: bad arguments");
+    return fail(ZP_EINVAL, "%s: bad arguments", name);
+  if (splits < 1 || splits > kMaxSplits)
+    return fail(ZP_EINVAL, "%s: splits %d outside [1, %d]", name, splits, kMaxSplits);
   if (num_reqs > 0 && (!out || !q || !block_tables || !seq_lens))
-    return fail(ZP_EINVAL, "zp_paged_decode: NULL device array");
-  if (!aligned16(out) || !aligned16(q))
-    return fail(ZP_EINVAL, "zp_paged_decode: out and q must be 16-byte aligned");
+    return fail(ZP_EINVAL, "%s: NULL device array", name);
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_new) || !aligned16(v_new))
+    return fail(ZP_EINVAL, "%s: out, q, k_new and v_new must be 16-byte aligned", name);
+  if ((k_new == nullptr) != (v_new == nullptr))
+    return fail(ZP_EINVAL, "%s: k_new and v_new go together", name);
   if (params->q_heads <= 0 || params->q_heads % pool->kv_heads)
-    return fail(ZP_EINVAL, "zp_paged_decode: q_heads not a multiple of kv_heads");
+    return fail(ZP_EINVAL, "%s: q_heads not a multiple of kv_heads", name);
   if (params->q_dtype != pool->dtype)
-    return fail(ZP_EUNSUPPORTED, "zp_paged_decode: q_dtype must equal pool dtype");
+    return fail(ZP_EUNSUPPORTED, "%s: q_dtype must equal pool dtype", name);
   if (!std::isfinite(params->sm_scale))
-    return fail(ZP_EINVAL, "zp_paged_decode: sm_scale must be finite");
+    return fail(ZP_EINVAL, "%s: sm_scale must be finite", name);
+  if (static_cast<int64_t>(num_reqs) * pool->layers * pool->kv_heads * splits >
+      (1ll << 31) - 4)
+    return fail(ZP_EINVAL, "%s: too many units", name);
+  if (splits > 1) {
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+      return fail(ZP_EWORKSPACE, "%s: workspace NULL or not 256-byte aligned", name);
+    if (workspace_bytes < decode_ws_bytes(pool, params, num_reqs, splits))
+      return fail(ZP_EWORKSPACE, "%s: workspace %zu < %zu bytes", name, workspace_bytes,
+                  decode_ws_bytes(pool, params, num_reqs, splits));
+  }
   if (num_reqs == 0) return ZP_OK;
   DecodeGeom g;
   g.R = num_reqs;
@@ -280,11 +307,64 @@ zp_status zp_paged_decode(float* out, const void* q, const zp_kv_pool* pool,
   g.max_blocks = max_blocks;
   g.dtype = pool->dtype;
   g.q_dtype = params->q_dtype;
+  g.splits = splits;
   g.scale_log2 = scale_log2(params, pool->head_dim);
+  DecodeIO io;
+  io.out = out;
+  io.q = q;
+  io.tables = block_tables;
+  io.seq_lens = seq_lens;
+  io.k_new = k_new;
+  io.v_new = v_new;
+  io.part_acc = static_cast<float*>(workspace);
+  io.part_mz = splits > 1 ? io.part_acc + static_cast<size_t>(num_reqs) * g.L * g.Hq *
+                                              splits * g.d
+                          : nullptr;
   timing_before(ZP_KERNEL_DECODE, stream);
-  st = launch_decode(g, out, q, *pool, block_tables, seq_lens, stream);
+  st = launch_decode(g, io, *pool, stream);
   timing_after(ZP_KERNEL_DECODE, stream);
   return st;
+}
+
+}  // namespace
+
+zp_status zp_paged_decode(float* out, const void* q, const zp_kv_pool* pool,
+                          const int32_t* block_tables, int32_t max_blocks,
+                          const int32_t* seq_lens, int32_t num_reqs,
+                          const zp_params* params, void* stream) {
+  return decode_common("zp_paged_decode", out, q, nullptr, nullptr, pool, block_tables,
+                       max_blocks, seq_lens, num_reqs, params, 1, nullptr, 0, stream);
+}
+
+zp_status zp_paged_decode_append(float* out, const void* q, const void* k_new,
+                                 const void* v_new, const zp_kv_pool* pool,
+                                 const int32_t* block_tables, int32_t max_blocks,
+                                 const int32_t* seq_lens, int32_t num_reqs,
+                                 const zp_params* params, void* stream) {
+  if (num_reqs > 0 && (!k_new || !v_new))
+    return fail(ZP_EINVAL, "zp_paged_decode_append: k_new and v_new are required");
+  return decode_common("zp_paged_decode_append", out, q, k_new, v_new, pool, block_tables,
+                       max_blocks, seq_lens, num_reqs, params, 1, nullptr, 0, stream);
+}
+
+zp_status zp_decode_workspace_bytes(const zp_kv_pool* pool, const zp_params* params,
+                                    int32_t num_reqs, int32_t splits, size_t* bytes) {
+  if (!pool || !params || !bytes || num_reqs < 0 || splits < 1 || splits > kMaxSplits ||
+      params->q_heads <= 0 || pool->layers < 1 || pool->head_dim < 1)
+    return fail(ZP_EINVAL, "zp_decode_workspace_bytes: bad arguments");
+  *bytes = splits > 1 ? decode_ws_bytes(pool, params, num_reqs, splits) : 0;
+  return ZP_OK;
+}
+
+zp_status zp_paged_decode_split(float* out, const void* q, const void* k_new,
+                                const void* v_new, const zp_kv_pool* pool,
+                                const int32_t* block_tables, int32_t max_blocks,
+                                const int32_t* seq_lens, int32_t num_reqs,
+                                const zp_params* params, int32_t splits, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  return decode_common("zp_paged_decode_split", out, q, k_new, v_new, pool, block_tables,
+                       max_blocks, seq_lens, num_reqs, params, splits, workspace,
+                       workspace_bytes, stream);
 }
 
 zp_status zp_capture_queries(void* q_window, const void* q, const int32_t* slot,

@@ -40,12 +40,21 @@ zp_status launch_capture(void* q_window, const void* q, const int32_t* slot,
                          void* stream);
 
 struct DecodeGeom {
-  int32_t R, L, Hkv, Hq, G, d, b, num_blocks, max_blocks, dtype, q_dtype;
+  int32_t R, L, Hkv, Hq, G, d, b, num_blocks, max_blocks, dtype, q_dtype, splits;
   float scale_log2;
 };
-zp_status launch_decode(const DecodeGeom& g, float* out, const void* q,
-                        const zp_kv_pool& pool, const int32_t* tables,
-                        const int32_t* seq_lens, void* stream);
+struct DecodeIO {
+  float* out;
+  const void* q;
+  const int32_t* tables;
+  const int32_t* seq_lens;
+  const void* k_new;   // null: no append
+  const void* v_new;
+  float* part_acc;     // splits > 1 only
+  float* part_mz;
+};
+zp_status launch_decode(const DecodeGeom& g, const DecodeIO& io, const zp_kv_pool& pool,
+                        void* stream);
 
 // Timing hooks: record an event pair around kernel `kind` when enabled.
 void timing_before(int kind, void* stream);

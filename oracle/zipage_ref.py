@@ -106,6 +106,8 @@ def widen(raw: np.ndarray, elem: str) -> np.ndarray:
         return bits.view(np.float32).astype(np.float64)
     if elem == "f32":
         return np.asarray(raw, dtype=np.float32).astype(np.float64)
+    if elem == "f64":  # float64 test inputs, already exact
+        return np.asarray(raw, dtype=np.float64)
     raise ValueError(f"unknown element type {elem!r}")
 
 
@@ -564,3 +566,25 @@ def paged_decode(q: np.ndarray, q_elem: str, pool_k: np.ndarray,
             res[h * G:(h + 1) * G] = decode_attention(qh, keys, vals)
         out[(r, l)] = res
     return out
+
+
+def paged_decode_append(q: np.ndarray, q_elem: str, k_new: np.ndarray,
+                        v_new: np.ndarray, pool_k: np.ndarray, pool_v: np.ndarray,
+                        elem: str, tables: np.ndarray, seq_lens: Sequence[int]
+                        ) -> Tuple[Dict[Tuple[int, int], np.ndarray], np.ndarray, np.ndarray]:
+    """A decode step that appends its token ([zh] §2.3: decoding extends the
+    request's tail block and attends over the paged cache). For every request
+    r the new rows k_new[r][l][h], v_new[r][l][h] (raw) are stored at logical
+    position seq_lens[r] of the block table in copies of the pools, then each
+    query head attends over the seq_lens[r] + 1 tokens. Returns the outputs
+    {(r, l): [Hq, d] float64} and the two updated pools (raw)."""
+    pk, pv = pool_k.copy(), pool_v.copy()
+    L, _, Hkv, b, _ = pool_k.shape
+    for r in range(q.shape[0]):
+        blk, slot = row_location(tables[r], int(seq_lens[r]), b)
+        for layer in range(L):
+            for h in range(Hkv):
+                pk[layer, blk, h, slot] = k_new[r, layer, h]
+                pv[layer, blk, h, slot] = v_new[r, layer, h]
+    out = paged_decode(q, q_elem, pk, pv, elem, tables, [int(x) + 1 for x in seq_lens])
+    return out, pk, pv

@@ -245,3 +245,34 @@ def test_window_ring_flag_is_accepted_by_validation():
     b = _batch(num_reqs=0)
     assert _compress(params=_params(flags=Z.ZP_WINDOW_RING), batch=b) == Z.ZP_OK
     assert _compress(params=_params(flags=1 << 7), batch=b) == Z.ZP_EINVAL
+
+
+def test_decode_append_and_split_reject_bad_arguments():
+    lib = Z.lib()
+    P = ctypes.byref
+    pool, prm = _pool(), _params()
+    # append needs both new rows
+    assert lib.zp_paged_decode_append(FAKE, FAKE, None, None, P(pool), FAKE, 4, FAKE, 2,
+                                      P(prm), None) == Z.ZP_EINVAL
+    assert lib.zp_paged_decode_append(FAKE, FAKE, FAKE, FAKE + 8, P(pool), FAKE, 4, FAKE,
+                                      2, P(prm), None) == Z.ZP_EINVAL   # misaligned
+    assert lib.zp_paged_decode_append(FAKE, FAKE, FAKE, FAKE, P(pool), FAKE, 4, FAKE, 0,
+                                      P(prm), None) == Z.ZP_OK          # empty batch
+
+    def split(splits, ws=0x100000, nbytes=1 << 30, k_new=None, v_new=None, R=2):
+        return lib.zp_paged_decode_split(FAKE, FAKE, k_new, v_new, P(pool), FAKE, 4, FAKE,
+                                         R, P(prm), splits, ws, nbytes, None)
+    assert split(0) == Z.ZP_EINVAL
+    assert split(257) == Z.ZP_EINVAL
+    assert split(4, ws=None) == Z.ZP_EWORKSPACE
+    assert split(4, ws=0x100010) == Z.ZP_EWORKSPACE                    # not 256-aligned
+    assert split(4, nbytes=100) == Z.ZP_EWORKSPACE
+    assert split(4, k_new=FAKE) == Z.ZP_EINVAL                          # k_new without v_new
+    assert split(4, R=0) == Z.ZP_OK
+
+
+def test_decode_workspace_formula():
+    pool, prm = _pool(), _params()
+    # R * layers * q_heads * splits * (head_dim + 2) floats; none for one split
+    assert Z.zp_decode_workspace_bytes(pool, prm, 3, 1) == 0
+    assert Z.zp_decode_workspace_bytes(pool, prm, 3, 5) == 3 * 2 * 8 * 5 * 130 * 4

@@ -155,3 +155,102 @@ def test_decode_rejects_bad_rows_on_device():
     for r in (1, 2, 3):
         assert bool((o[r] == 123.0).all()), f"request {r} was written"
     assert bool(torch.isfinite(o[0]).all()) and not bool((o[0] == 123.0).any())
+
+
+# ------------------------------------------------------ append, split-K ---
+
+def _append_case(spec, lens, seed, splits=1):
+    dev = "cuda"
+    wl = synth.make(spec, device=dev)
+    R, L, H = spec.requests, spec.layers, spec.kv_heads
+    lens = np.asarray(lens, dtype=np.int32)
+    q = synth.decode_queries(spec, R, dev, seed)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed + 1)
+    k_new = torch.randn((R, L, H, spec.head_dim), generator=gen, device=dev).to(wl.k_pool.dtype)
+    v_new = torch.randn((R, L, H, spec.head_dim), generator=gen, device=dev).to(wl.k_pool.dtype)
+    dt = Z.ZP_BF16 if spec.dtype == "bf16" else Z.ZP_F32
+    params = Z.make_params(spec.n_max, spec.window, spec.q_heads, dt)
+    pool = Z.make_pool(wl.k_pool, wl.v_pool)
+    pk0, pv0 = synth.raw_numpy(wl.k_pool), synth.raw_numpy(wl.v_pool)
+    out = torch.full((R, L, spec.q_heads, spec.head_dim), float("nan"),
+                     dtype=torch.float32, device=dev)
+    tab = torch.from_numpy(wl.tables).to(dev)
+    lens_dev = torch.from_numpy(lens).to(dev)
+    if splits == 1:
+        Z.zp_paged_decode_append(out, q, k_new, v_new, pool, tab, lens_dev, params)
+    else:
+        nbytes = Z.zp_decode_workspace_bytes(pool, params, R, splits)
+        ws = torch.empty((nbytes + 255) // 256 * 64, dtype=torch.int32, device=dev)
+        Z.zp_paged_decode_split(out, q, pool, tab, lens_dev, params, splits, ws,
+                                k_new=k_new, v_new=v_new)
+    torch.cuda.synchronize()
+    ref, rk, rv = O.paged_decode_append(synth.raw_numpy(q), spec.dtype,
+                                        synth.raw_numpy(k_new), synth.raw_numpy(v_new),
+                                        pk0, pv0, spec.dtype, wl.tables, lens)
+    assert synth.raw_numpy(wl.k_pool).tobytes() == rk.tobytes(), "K pool after append"
+    assert synth.raw_numpy(wl.v_pool).tobytes() == rv.tobytes(), "V pool after append"
+    got = out.cpu().numpy().astype(np.float64)
+    for (r, l), want in ref.items():
+        err = np.abs(got[r, l] - want)
+        assert np.all(err <= RTOL * np.abs(want) + ATOL), (r, l, lens[r], err.max())
+
+
+APPEND_SPEC = synth.scaled(synth.EIGHT_B, requests=7, layers=2, kv_heads=2,
+                           q_heads=8, n_max=6, pool_blocks=7 * 6)
+
+
+def test_decode_append_matches_oracle():
+    # cached lengths 0 (first token), 15 (fills a block), 16 (opens one),
+    # 31, 47, 95 (last slot of the table) and 50
+    _append_case(APPEND_SPEC, [0, 15, 16, 31, 47, 95, 50], seed=31)
+
+
+@pytest.mark.parametrize("splits", [2, 5, 64])
+def test_decode_split_matches_oracle(splits):
+    # more splits than blocks leaves some splits empty
+    spec = synth.scaled(synth.EIGHT_B, requests=3, layers=2, kv_heads=2, q_heads=8,
+                        n_max=40, pool_blocks=3 * 40)
+    dev = "cuda"
+    wl = synth.make(spec, device=dev)
+    R, L = spec.requests, spec.layers
+    lens = np.array([640, 17, 1], dtype=np.int32)
+    q = synth.decode_queries(spec, R, dev, 41)
+    params = Z.make_params(spec.n_max, spec.window, spec.q_heads, Z.ZP_BF16)
+    pool = Z.make_pool(wl.k_pool, wl.v_pool)
+    nbytes = Z.zp_decode_workspace_bytes(pool, params, R, splits)
+    ws = torch.empty((nbytes + 255) // 256 * 64, dtype=torch.int32, device=dev)
+    out = torch.full((R, L, spec.q_heads, spec.head_dim), float("nan"),
+                     dtype=torch.float32, device=dev)
+    tab = torch.from_numpy(wl.tables).to(dev)
+    Z.zp_paged_decode_split(out, q, pool, tab, torch.from_numpy(lens).to(dev), params,
+                            splits, ws)
+    torch.cuda.synchronize()
+    ref = O.paged_decode(synth.raw_numpy(q), spec.dtype, synth.raw_numpy(wl.k_pool),
+                         synth.raw_numpy(wl.v_pool), spec.dtype, wl.tables, lens)
+    got = out.cpu().numpy().astype(np.float64)
+    for (r, l), want in ref.items():
+        err = np.abs(got[r, l] - want)
+        assert np.all(err <= RTOL * np.abs(want) + ATOL), (r, l, err.max())
+
+
+def test_decode_split_with_append_matches_oracle():
+    _append_case(APPEND_SPEC, [0, 15, 16, 31, 47, 95, 50], seed=32, splits=3)
+
+
+def test_decode_split_rejects_small_workspace():
+    spec = APPEND_SPEC
+    dev = "cuda"
+    wl = synth.make(spec, device=dev)
+    params = Z.make_params(spec.n_max, spec.window, spec.q_heads, Z.ZP_BF16)
+    pool = Z.make_pool(wl.k_pool, wl.v_pool)
+    R = spec.requests
+    nbytes = Z.zp_decode_workspace_bytes(pool, params, R, 4)
+    ws = torch.empty(nbytes // 4 - 64, dtype=torch.int32, device=dev)
+    out = torch.zeros((R, spec.layers, spec.q_heads, spec.head_dim), device=dev)
+    with pytest.raises(Z.ZipageError) as ei:
+        Z.zp_paged_decode_split(out, synth.decode_queries(spec, R, dev, 1), pool,
+                                torch.from_numpy(wl.tables).to(dev),
+                                torch.full((R,), 20, dtype=torch.int32, device=dev),
+                                params, 4, ws)
+    assert ei.value.status == Z.ZP_EWORKSPACE

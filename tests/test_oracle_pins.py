@@ -477,3 +477,45 @@ def test_ring_window_scores_like_the_linear_window():
     a1 = O.window_attention(lin, keys, n, True)
     a2 = O.window_attention(O.window_from_ring(ring[0, 0], n, w), keys, n, True)
     assert np.array_equal(a1, a2)
+
+
+# ---------------------------------------------------------------------------
+# decode with an appended token ([zh] §2.3)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("lens", [[0, 5, 16, 31], [15, 1, 32, 47]])
+def test_decode_append_equals_sdpa_over_cache_plus_new_token(lens):
+    """The appended token lands in the slot its position names, nothing else
+    in the pools changes, and each head's output is torch SDPA over the cached
+    rows followed by the new one."""
+    rng = np.random.default_rng(sum(lens))
+    R, L, Hkv, G, b, d, nb = len(lens), 2, 2, 2, 16, 8, 3
+    Hq = Hkv * G
+    pool_k = rng.standard_normal((L, R * nb, Hkv, b, d))
+    pool_v = rng.standard_normal((L, R * nb, Hkv, b, d))
+    tables = rng.permutation(R * nb).reshape(R, nb)
+    q = rng.standard_normal((R, L, Hq, d))
+    k_new = rng.standard_normal((R, L, Hkv, d))
+    v_new = rng.standard_normal((R, L, Hkv, d))
+    out, pk, pv = O.paged_decode_append(q, "f64", k_new, v_new, pool_k, pool_v,
+                                        "f64", tables, lens)
+    mask = np.ones(pk.shape, dtype=bool)
+    for r, n in enumerate(lens):
+        mask[:, tables[r, n // b], :, n % b] = False
+    assert np.array_equal(pk[mask], pool_k[mask])       # every other row unchanged
+    assert np.array_equal(pv[mask], pool_v[mask])
+    for r, n in enumerate(lens):
+        blk, slot = tables[r, n // b], n % b
+        assert np.array_equal(pk[:, blk, :, slot], k_new[r])
+        assert np.array_equal(pv[:, blk, :, slot], v_new[r])
+        for layer in range(L):
+            for h in range(Hkv):
+                rows = [pool_k[layer, tables[r, t // b], h, t % b] for t in range(n)]
+                vrows = [pool_v[layer, tables[r, t // b], h, t % b] for t in range(n)]
+                keys = np.array(rows + [k_new[r, layer, h]])
+                vals = np.array(vrows + [v_new[r, layer, h]])
+                want = torch.nn.functional.scaled_dot_product_attention(
+                    torch.from_numpy(q[r, layer, h * G:(h + 1) * G])[None],
+                    torch.from_numpy(keys)[None], torch.from_numpy(vals)[None])[0].numpy()
+                np.testing.assert_allclose(out[(r, layer)][h * G:(h + 1) * G], want,
+                                           rtol=1e-12, atol=1e-14)
