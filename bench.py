@@ -23,7 +23,8 @@ the line reports compressed tokens/s under overlap plus the three times.
 With --workload capture_8b_32L_32q it times query-window capture alone (128
 slot-holding requests x 32 layers x 32 query heads of 128, w = 32); with
 --workload decode_8b_32L_8kv_32q the decode consumer (plain, with append, and
-split-K on a long-context small batch).
+split-K on a long-context small batch); with --workload redundancy_ablation_8b
+the all-pairs redundancy against the whole compression step on 1024 units.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        [--cpu-seconds S] [--no-cpu]
@@ -434,6 +435,69 @@ def run_decode(args):
     }), flush=True)
 
 
+def run_redundancy_ablation(args):
+    """All-pairs redundancy (the score lightning replaces) against the whole
+    compression step on the same units: 4 requests x 32 layers x 8 KV heads of
+    the 8B-like workload, N = 4096."""
+    import torch
+    import kv_cache_compression_paged_amd as Z
+    from kv_cache_compression_paged_amd import synth
+    spec = synth.scaled(synth.EIGHT_B, requests=4, pool_blocks=4 * 256)
+    dev = "cuda"
+    wl = synth.make(spec, device=dev)
+    R, L, H, d, n = spec.requests, spec.layers, spec.kv_heads, spec.head_dim, spec.n_tokens
+    U = R * L * H
+    params = Z.make_params(spec.n_max, spec.window, spec.q_heads, Z.ZP_BF16)
+    pool = Z.make_pool(wl.k_pool, wl.v_pool)
+    tab = torch.from_numpy(wl.tables).to(dev)
+    batch = Z.DeviceBatch(slot=torch.arange(R, dtype=torch.int32, device=dev),
+                          n_tokens=torch.full((R,), n, dtype=torch.int32, device=dev),
+                          src_table=tab, dst_table=tab.clone(),
+                          n_pinned=torch.zeros(R, dtype=torch.int32, device=dev),
+                          num_slots=R, n_cap=n)
+    ws = Z.alloc_workspace(pool, params, R, dev)
+    red_b = torch.empty((U, n), device=dev)
+    red_a = torch.empty((U, n), device=dev)
+    out = Z.alloc_outputs(U, spec.keep, n, dev)
+    reps = max(args.steps, 1)
+
+    def timed(fn, kind):
+        fn()
+        torch.cuda.synchronize()
+        Z.timing_read()
+        Z.timing_enable(True)
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        Z.timing_enable(False)
+        cnt, tot = Z.timing_read()[kind]
+        return tot / cnt
+
+    t_full = timed(lambda: Z.zp_redundancy_full(red_b, pool, batch, params, ws, red_all=red_a),
+                   "redundancy_full")
+    t_comp = timed(lambda: Z.zp_compress(pool, batch, wl.q_window, wl.global_scores, params,
+                                         out, ws), "compress")
+    if Z.zp_workspace_error(ws) != Z.ZP_OK:
+        raise RuntimeError("device error in the ablation run")
+    flops_full = U * 2.0 * n * n * d
+    print(json.dumps({
+        "metric": "all-pairs redundancy vs lightning (whole compression step), same units",
+        "value": round(t_full / t_comp, 2), "unit": "x slower than the full compression",
+        "n_gpus": 1, "steps": reps, "warmup": 1, "ms_per_step": round(t_full, 4),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "redundancy_ablation_8b", "units": U, "tokens": n,
+                   "head_dim": d},
+        "all_pairs_ms": round(t_full, 4), "compress_ms": round(t_comp, 4),
+        "all_pairs_TFLOPs": round(flops_full / (t_full * 1e-3) / 1e12, 1),
+        "roofline": {"bound": "mfma", "kernel": "redundancy_full",
+                     "achieved": round(flops_full / (t_full * 1e-3) / 1e12, 1),
+                     "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": round(flops_full / (t_full * 1e-3) / 1e12 / 2500.0, 4),
+                     "traffic": None, "alg_bytes_per_launch": None},
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -453,6 +517,9 @@ def main():
         return
     if args.workload == "decode_8b_32L_8kv_32q":
         run_decode(args)
+        return
+    if args.workload == "redundancy_ablation_8b":
+        run_redundancy_ablation(args)
         return
     spec = synth.SPECS[args.workload]
     if spec.compress_groups > 1:

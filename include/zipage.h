@@ -239,6 +239,22 @@ zp_status zp_paged_decode_split(float* out, const void* q, const void* k_new,
                                 const zp_params* params, int32_t splits, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/* All-pairs key redundancy, an ablation of the lightning score ([zh] §2.1,
+ * [fr] §2.E: the original score compared every pair of cached keys, O(N^2 b^2)
+ * for N blocks of b; lightning keeps the pairs inside a block, O(N b^2)).
+ * For every unit of `batch` the full n x n cosine matrix of its keys is
+ * formed (norm products clamped at 1e-8, the diagonal dropped) and each token
+ * gets red_block[u][t], the mean over the other tokens of its block (equal
+ * to zp_compress's red, up to rounding), and, when red_all is not NULL,
+ * red_all[u][t], the mean over all other tokens. Rows [0, n) of
+ * [U][n_cap] fp32 outputs are written; only src_table and n_tokens of the
+ * batch are read. Nothing is moved or selected. workspace: as zp_compress
+ * (its error word; a bad table entry gives ZP_EDEVICE there).
+ * Errors: as zp_compress. */
+zp_status zp_redundancy_full(float* red_block, float* red_all, const zp_kv_pool* pool,
+                             const zp_batch* batch, const zp_params* params,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 /* Query-window capture, the step before compression ([zh] §2.2, [de] §2: only
  * requests that hold a query slot keep their recent queries; [zh] §2.1: the
  * last w queries score the cache). For every request r with a slot
@@ -327,7 +343,8 @@ int32_t zp_plan_targets(const zp_plan* plan, int32_t* ids, int32_t cap);
 #define ZP_KERNEL_GLOBAL   1  /* global-score update                         */
 #define ZP_KERNEL_DECODE   2  /* paged decode                                */
 #define ZP_KERNEL_CAPTURE  3  /* query-window capture                        */
-#define ZP_KERNEL_KINDS    4
+#define ZP_KERNEL_REDUNDANCY_FULL 4  /* all-pairs redundancy (ablation)      */
+#define ZP_KERNEL_KINDS    5
 
 zp_status zp_timing_enable(int32_t enable);
 zp_status zp_timing_read(int32_t* launches /*[ZP_KERNEL_KINDS]*/,

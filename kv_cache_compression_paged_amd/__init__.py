@@ -41,13 +41,16 @@ ZP_KERNEL_COMPRESS = 0
 ZP_KERNEL_GLOBAL = 1
 ZP_KERNEL_DECODE = 2
 ZP_KERNEL_CAPTURE = 3
-ZP_KERNEL_KINDS = 4
-KERNEL_NAMES = ("compress", "global_update", "paged_decode", "capture")
+ZP_KERNEL_REDUNDANCY_FULL = 4
+ZP_KERNEL_KINDS = 5
+KERNEL_NAMES = ("compress", "global_update", "paged_decode", "capture",
+                "redundancy_full")
 
 EXPORTED = (
     "zp_compress_workspace_bytes", "zp_compress", "zp_update_global",
     "zp_workspace_error", "zp_paged_decode", "zp_paged_decode_append",
     "zp_decode_workspace_bytes", "zp_paged_decode_split", "zp_capture_queries",
+    "zp_redundancy_full",
     "zp_bm_create", "zp_bm_destroy",
     "zp_bm_alloc", "zp_bm_incref", "zp_bm_release", "zp_bm_free_count",
     "zp_bm_refcount", "zp_bm_free_list", "zp_bm_plan_compress",
@@ -120,6 +123,7 @@ def lib() -> ctypes.CDLL:
         "zp_workspace_error": (I32, [P, P, P]),
         "zp_paged_decode": (I32, [P, P, P, P, I32, P, I32, P, P]),
         "zp_capture_queries": (I32, [P, P, P, P, I32, I32, I32, I32, P, P]),
+        "zp_redundancy_full": (I32, [P, P, P, P, P, P, U, P]),
         "zp_paged_decode_append": (I32, [P, P, P, P, P, P, I32, P, I32, P, P]),
         "zp_decode_workspace_bytes": (I32, [P, P, I32, I32, P]),
         "zp_paged_decode_split": (I32, [P, P, P, P, P, P, I32, P, I32, P, I32, P, U, P]),
@@ -327,6 +331,15 @@ def zp_paged_decode_split(out, q, pool: KVPool, block_tables, seq_lens,
            "zp_paged_decode_split")
 
 
+def zp_redundancy_full(red_block, pool: KVPool, batch: DeviceBatch, params: Params,
+                       workspace, red_all=None, stream=None) -> None:
+    b = batch.struct()
+    _check(lib().zp_redundancy_full(_ptr(red_block), _ptr(red_all), ctypes.byref(pool),
+                                    ctypes.byref(b), ctypes.byref(params), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(),
+                                    _stream_handle(stream)), "zp_redundancy_full")
+
+
 def zp_capture_queries(q_window, q, slot, pos, params: Params,
                        stream=None) -> None:
     """q_window [slots][L][w][Hq][d], q [R][L][Hq][d] (same dtype), slot and
@@ -453,7 +466,7 @@ __all__: Tuple[str, ...] = (
     "alloc_workspace", "zp_compress_workspace_bytes", "zp_compress",
     "zp_update_global", "zp_workspace_error", "zp_paged_decode",
     "zp_capture_queries", "zp_paged_decode_append", "zp_decode_workspace_bytes",
-    "zp_paged_decode_split",
+    "zp_paged_decode_split", "zp_redundancy_full",
     "timing_enable", "timing_read", "BlockManager", "Plan", "version",
     "EXPORTED",
 )

@@ -367,6 +367,24 @@ zp_status zp_paged_decode_split(float* out, const void* q, const void* k_new,
                        workspace_bytes, stream);
 }
 
+zp_status zp_redundancy_full(float* red_block, float* red_all, const zp_kv_pool* pool,
+                             const zp_batch* batch, const zp_params* params,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  CompressGeom g;
+  zp_status st = make_geom(pool, params, batch, &g);
+  if (st != ZP_OK) return st;
+  if (!red_block) return fail(ZP_EINVAL, "zp_redundancy_full: red_block is required");
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) ||
+      workspace_bytes < kWsHeader)
+    return fail(ZP_EWORKSPACE, "zp_redundancy_full: workspace missing, misaligned or small");
+  if (g.R == 0) return ZP_OK;
+  timing_before(ZP_KERNEL_REDUNDANCY_FULL, stream);
+  st = launch_redundancy_full(g, *pool, *batch, red_block, red_all,
+                              static_cast<int32_t*>(workspace), stream);
+  timing_after(ZP_KERNEL_REDUNDANCY_FULL, stream);
+  return st;
+}
+
 zp_status zp_capture_queries(void* q_window, const void* q, const int32_t* slot,
                              const int32_t* pos, int32_t num_reqs, int32_t layers,
                              int32_t num_slots, int32_t head_dim,

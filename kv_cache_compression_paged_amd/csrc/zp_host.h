@@ -34,6 +34,9 @@ zp_status launch_global(const CompressGeom& g, float* global_scores,
                         const zp_batch& batch, const int32_t* keep,
                         const float* attn, void* stream);
 
+zp_status launch_redundancy_full(const CompressGeom& g, const zp_kv_pool& pool,
+                                 const zp_batch& batch, float* red_block, float* red_all,
+                                 int32_t* err, void* stream);
 zp_status launch_capture(void* q_window, const void* q, const int32_t* slot,
                          const int32_t* pos, int32_t num_reqs, int32_t layers,
                          int32_t num_slots, int32_t window, int32_t row_bytes,

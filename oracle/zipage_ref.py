@@ -232,6 +232,28 @@ def lightning_redundancy(keys: np.ndarray, b: int, n: int) -> np.ndarray:
     return red
 
 
+def redundancy_all_pairs(keys: np.ndarray, b: int, n: int
+                         ) -> Tuple[np.ndarray, np.ndarray]:
+    """The all-pairs key similarity that the lightning score replaces
+    ([zh §2.1], [fr §2.E]: the original score was O(N^2 b^2) for N blocks of
+    b tokens). The full n x n cosine matrix is formed, the diagonal dropped,
+    and two means taken per token: over the other tokens of its block (this
+    equals the lightning score, the reading that makes lightning an exact
+    speed-up) and over all other tokens. Same clamp as lightning: the norm
+    product is taken at least 1e-8; a lone token scores 0."""
+    if keys.shape[0] != n:
+        raise ValueError("keys must hold n rows")
+    norms = np.sqrt((keys * keys).sum(axis=1))
+    cos = (keys @ keys.T) / np.maximum(np.outer(norms, norms), 1e-8)
+    np.fill_diagonal(cos, 0.0)
+    blk = np.arange(n) // b
+    same = blk[:, None] == blk[None, :]
+    cnt = np.bincount(blk)[blk]
+    red_block = np.where(cnt >= 2, (cos * same).sum(axis=1) / np.maximum(cnt - 1, 1), 0.0)
+    red_all = cos.sum(axis=1) / (n - 1) if n >= 2 else np.zeros(n)
+    return red_block, red_all
+
+
 def combine_scores(attn: np.ndarray, glob: np.ndarray, red: np.ndarray,
                    p: Params) -> np.ndarray:
     """s_t = w_attn*attn_t + w_global*global_t - w_red*red_t.

@@ -519,3 +519,23 @@ def test_decode_append_equals_sdpa_over_cache_plus_new_token(lens):
                     torch.from_numpy(keys)[None], torch.from_numpy(vals)[None])[0].numpy()
                 np.testing.assert_allclose(out[(r, layer)][h * G:(h + 1) * G], want,
                                            rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# the all-pairs redundancy kept as an ablation ([zh] §2.1, [fr] §2.E)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,b,d", [(64, 16, 32), (50, 16, 8), (33, 4, 128), (17, 16, 4)])
+def test_all_pairs_redundancy_pins(n, b, d):
+    rng = np.random.default_rng(7 * n + d)
+    keys = rng.standard_normal((n, d))
+    red_block, red_all = O.redundancy_all_pairs(keys, b, n)
+    # the same-block restriction is the lightning score (loops, per block)
+    np.testing.assert_allclose(red_block, O.lightning_redundancy(keys, b, n),
+                               rtol=1e-12, atol=1e-14)
+    # the all-token mean against torch's pairwise cosine similarity
+    t = torch.from_numpy(keys)
+    cos = torch.nn.functional.cosine_similarity(t[:, None, :], t[None, :, :], dim=-1,
+                                                eps=0.0).numpy()
+    want = (cos.sum(axis=1) - np.diag(cos)) / (n - 1)
+    np.testing.assert_allclose(red_all, want, rtol=1e-10, atol=1e-12)
