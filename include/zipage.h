@@ -115,6 +115,13 @@ typedef struct {
  *                     source block, entry n_max-1 is any block (the new tail).
  *   n_pinned[R]    -- S, the leading shared blocks, kept whole and never
  *                     written ([zh] §2.2, [de] §2, [fr] §2.C).
+ *   seq_pos[R]     -- optional (NULL: n_tokens), read with ZP_WINDOW_RING
+ *                     only: sequence position P of the request's next token,
+ *                     the position zp_capture_queries rings by. Window row i
+ *                     (the i-th of the last w queries) is ring row
+ *                     (P - w + i) mod w; P >= w. After a compression the
+ *                     cache holds fewer tokens than the sequence, so P and
+ *                     n_tokens differ.
  * Host fields: num_reqs, max_blocks, num_slots (rows of q_window and of
  * global_scores) and n_cap (length of a global-score row and of the attn /
  * red / score output rows; n_cap <= 16384). */
@@ -128,6 +135,7 @@ typedef struct {
   const int32_t* src_table;
   const int32_t* dst_table;
   const int32_t* n_pinned;
+  const int32_t* seq_pos;
 } zp_batch;
 
 /* Outputs of zp_compress, one row per unit u = (r*layers + l)*kv_heads + h.
@@ -331,6 +339,85 @@ zp_status zp_bm_abort(zp_bm* bm, zp_plan* plan);
 int32_t zp_plan_freed(const zp_plan* plan, int32_t* ids, int32_t cap);
 /* Targets the plan popped, in pop order; returns their number. */
 int32_t zp_plan_targets(const zp_plan* plan, int32_t* ids, int32_t cap);
+
+/* ---------------------------------------------------------------------------
+ * Hybrid scheduling (host, no GPU calls): query slots, slot-free decoding,
+ * preemption and a restricted mode ([zh] §2.2, [de] §2, [fr] §2.B), with
+ * compression running beside decoding ([zh] §2.1, [fr] §2.D). The scheduler
+ * owns a block manager of num_blocks blocks. Each zp_sched_step plans one
+ * step in admission order:
+ *   1. the first query_slots (M) running requests hold the M query slots;
+ *   2. a slot holder with n >= N_max*b cached tokens that has captured w
+ *      queries compresses (and does not decode) this step; target blocks of
+ *      a shared-prefix compression are taken first, preempting slot-free
+ *      requests if needed;
+ *   3. every other request decodes one token, except a slot-free request
+ *      with n >= N_max*b - w (its queries would have to be captured: it waits
+ *      for a slot). A token that opens a block takes one from the free list;
+ *      when it is empty the most recently admitted slot-free request is
+ *      preempted (its blocks are released and it returns to the front of the
+ *      waiting queue, to be prefilled again with prompt + generated tokens).
+ *      With no slot-free request left the step is restricted: requests
+ *      without a block wait and nothing is admitted;
+ *   4. waiting requests are admitted FIFO while blocks last; a prompt of at
+ *      least N_max*b - w tokens is admitted only if it gets a slot. Prompts of
+ *      a prefix group share the group's cached prefix blocks.
+ * The caller runs the plan's GPU work (prefill of admitted requests, query
+ * capture and decode with append for the decode set, zp_compress +
+ * zp_update_global for the compress set with dst tables and n_pinned from the
+ * plan), then calls zp_sched_complete. Plan arrays are host memory owned by
+ * the scheduler, valid until the next zp_sched_step; tables are rows of
+ * max_blocks (compress_dst: rows of n_max), padded with -1. Not thread-safe.
+ * ------------------------------------------------------------------------ */
+typedef struct zp_sched zp_sched;
+
+typedef struct {
+  int32_t num_blocks;   /* blocks of the pool                               */
+  int32_t block_size;   /* b                                                */
+  int32_t n_max;        /* N_max                                            */
+  int32_t window;       /* w                                                */
+  int32_t query_slots;  /* M                                                */
+  int32_t max_running;  /* cap on running requests                          */
+  int32_t max_blocks;   /* table row width; >= ceil((prompt+gen)/b) of all  */
+} zp_sched_config;
+
+typedef struct {
+  int32_t restricted, max_blocks;
+  int32_t num_admit;          /* prefill: write K/V of tokens [shared, len)  */
+  const int32_t *admit_id, *admit_len, *admit_slot, *admit_table, *admit_shared;
+  int32_t num_new_slots;      /* slots handed out: clear ring and global row */
+  const int32_t* new_slot;
+  int32_t num_decode;         /* one token each at cache position len,       */
+  const int32_t *decode_id, *decode_slot, *decode_len, *decode_pos,
+      *decode_table;          /* sequence position pos (ring row pos mod w)  */
+  int32_t num_compress;       /* n tokens, next sequence position pos        */
+  const int32_t *compress_id, *compress_slot, *compress_len, *compress_pos,
+      *compress_src, *compress_dst, *compress_pinned;
+  int32_t num_preempt;
+  const int32_t* preempt_id;
+} zp_sched_plan;
+
+typedef struct {
+  int64_t steps, tokens, compressions, preemptions, restricted_steps, admitted,
+      finished;
+  int32_t running, waiting, free_blocks;
+} zp_sched_stats;
+
+zp_sched* zp_sched_create(const zp_sched_config* cfg);   /* NULL on error   */
+void zp_sched_destroy(zp_sched* s);
+zp_bm* zp_sched_block_manager(zp_sched* s);              /* for inspection  */
+/* A cached shared prefix of `blocks` blocks (1 <= blocks < n_max): allocated
+ * now, one reference held by the cache for the scheduler's lifetime; its ids
+ * are returned so the caller can fill their K/V. */
+zp_status zp_sched_add_prefix(zp_sched* s, int32_t blocks, int32_t* group,
+                              int32_t* block_ids);
+/* Queue a request (ids unique, >= 0); group -1 or a prefix group whose
+ * prefix the prompt starts with. */
+zp_status zp_sched_submit(zp_sched* s, int32_t req_id, int32_t prompt_len,
+                          int32_t gen_len, int32_t group);
+zp_status zp_sched_step(zp_sched* s, zp_sched_plan* plan);
+zp_status zp_sched_complete(zp_sched* s);
+zp_status zp_sched_get_stats(const zp_sched* s, zp_sched_stats* stats);
 
 /* ---------------------------------------------------------------------------
  * Kernel timing for measurement: while enabled, zp_compress,

@@ -51,6 +51,9 @@ EXPORTED = (
     "zp_workspace_error", "zp_paged_decode", "zp_paged_decode_append",
     "zp_decode_workspace_bytes", "zp_paged_decode_split", "zp_capture_queries",
     "zp_redundancy_full",
+    "zp_sched_create", "zp_sched_destroy", "zp_sched_block_manager",
+    "zp_sched_add_prefix", "zp_sched_submit", "zp_sched_step", "zp_sched_complete",
+    "zp_sched_get_stats",
     "zp_bm_create", "zp_bm_destroy",
     "zp_bm_alloc", "zp_bm_incref", "zp_bm_release", "zp_bm_free_count",
     "zp_bm_refcount", "zp_bm_free_list", "zp_bm_plan_compress",
@@ -86,7 +89,7 @@ class BatchStruct(ctypes.Structure):
                 ("num_slots", ctypes.c_int32), ("n_cap", ctypes.c_int32),
                 ("slot", ctypes.c_void_p), ("n_tokens", ctypes.c_void_p),
                 ("src_table", ctypes.c_void_p), ("dst_table", ctypes.c_void_p),
-                ("n_pinned", ctypes.c_void_p)]
+                ("n_pinned", ctypes.c_void_p), ("seq_pos", ctypes.c_void_p)]
 
 
 class CompressOut(ctypes.Structure):
@@ -124,6 +127,14 @@ def lib() -> ctypes.CDLL:
         "zp_paged_decode": (I32, [P, P, P, P, I32, P, I32, P, P]),
         "zp_capture_queries": (I32, [P, P, P, P, I32, I32, I32, I32, P, P]),
         "zp_redundancy_full": (I32, [P, P, P, P, P, P, U, P]),
+        "zp_sched_create": (P, [P]),
+        "zp_sched_destroy": (None, [P]),
+        "zp_sched_block_manager": (P, [P]),
+        "zp_sched_add_prefix": (I32, [P, I32, P, P]),
+        "zp_sched_submit": (I32, [P, I32, I32, I32, I32]),
+        "zp_sched_step": (I32, [P, P]),
+        "zp_sched_complete": (I32, [P]),
+        "zp_sched_get_stats": (I32, [P, P]),
         "zp_paged_decode_append": (I32, [P, P, P, P, P, P, I32, P, I32, P, P]),
         "zp_decode_workspace_bytes": (I32, [P, P, I32, I32, P]),
         "zp_paged_decode_split": (I32, [P, P, P, P, P, P, I32, P, I32, P, I32, P, U, P]),
@@ -215,12 +226,14 @@ class DeviceBatch:
     n_pinned: object
     num_slots: int
     n_cap: int
+    seq_pos: object = None     # [R] int32, ring position base (ZP_WINDOW_RING)
 
     def struct(self) -> BatchStruct:
         R, mb = self.src_table.shape
         return BatchStruct(R, mb, self.num_slots, self.n_cap, _ptr(self.slot),
                            _ptr(self.n_tokens), _ptr(self.src_table),
-                           _ptr(self.dst_table), _ptr(self.n_pinned))
+                           _ptr(self.dst_table), _ptr(self.n_pinned),
+                           _ptr(self.seq_pos))
 
 
 @dataclass
@@ -456,6 +469,129 @@ class BlockManager:
         plan.handle = None
 
 
+class SchedConfig(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int32) for name in
+                ("num_blocks", "block_size", "n_max", "window", "query_slots",
+                 "max_running", "max_blocks")]
+
+
+_PI = ctypes.POINTER(ctypes.c_int32)
+
+
+class SchedPlanStruct(ctypes.Structure):
+    _fields_ = [("restricted", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
+                ("num_admit", ctypes.c_int32),
+                ("admit_id", _PI), ("admit_len", _PI), ("admit_slot", _PI),
+                ("admit_table", _PI), ("admit_shared", _PI),
+                ("num_new_slots", ctypes.c_int32), ("new_slot", _PI),
+                ("num_decode", ctypes.c_int32),
+                ("decode_id", _PI), ("decode_slot", _PI), ("decode_len", _PI),
+                ("decode_pos", _PI), ("decode_table", _PI),
+                ("num_compress", ctypes.c_int32),
+                ("compress_id", _PI), ("compress_slot", _PI), ("compress_len", _PI),
+                ("compress_pos", _PI), ("compress_src", _PI), ("compress_dst", _PI),
+                ("compress_pinned", _PI),
+                ("num_preempt", ctypes.c_int32), ("preempt_id", _PI)]
+
+
+class SchedStatsStruct(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in
+                ("steps", "tokens", "compressions", "preemptions", "restricted_steps",
+                 "admitted", "finished")] + \
+               [(n, ctypes.c_int32) for n in ("running", "waiting", "free_blocks")]
+
+
+@dataclass
+class SchedPlan:
+    """One planned step, copied out of the scheduler (numpy int32 arrays;
+    table rows padded with -1)."""
+    restricted: bool
+    admit_id: np.ndarray
+    admit_len: np.ndarray
+    admit_slot: np.ndarray
+    admit_table: np.ndarray       # [A][max_blocks]
+    admit_shared: np.ndarray
+    new_slot: np.ndarray
+    decode_id: np.ndarray
+    decode_slot: np.ndarray
+    decode_len: np.ndarray
+    decode_pos: np.ndarray
+    decode_table: np.ndarray      # [D][max_blocks]
+    compress_id: np.ndarray
+    compress_slot: np.ndarray
+    compress_len: np.ndarray
+    compress_pos: np.ndarray
+    compress_src: np.ndarray      # [C][max_blocks]
+    compress_dst: np.ndarray      # [C][n_max]
+    compress_pinned: np.ndarray
+    preempt_id: np.ndarray
+
+
+def _arr(ptr, n, shape=None) -> np.ndarray:
+    if n == 0:
+        return np.zeros(shape if shape else (0,), dtype=np.int32)
+    a = np.ctypeslib.as_array(ptr, shape=(n,)).copy()
+    return a.reshape(shape) if shape else a
+
+
+class Scheduler:
+    """Hybrid compression/decode scheduler of the library (host only)."""
+
+    def __init__(self, num_blocks: int, block_size: int, n_max: int, window: int,
+                 query_slots: int, max_running: int, max_blocks: int):
+        self.cfg = SchedConfig(num_blocks, block_size, n_max, window, query_slots,
+                               max_running, max_blocks)
+        h = lib().zp_sched_create(ctypes.byref(self.cfg))
+        if not h:
+            raise ZipageError(ZP_EINVAL, "zp_sched_create",
+                              lib().zp_last_error().decode())
+        self.h = h
+
+    def __del__(self):
+        if getattr(self, "h", None) and _lib is not None:
+            _lib.zp_sched_destroy(self.h)
+            self.h = None
+
+    def add_prefix(self, blocks: int):
+        group = ctypes.c_int32(0)
+        ids = np.zeros(blocks, dtype=np.int32)
+        _check(lib().zp_sched_add_prefix(self.h, blocks, ctypes.byref(group),
+                                         _np_ptr(ids)), "zp_sched_add_prefix")
+        return group.value, ids
+
+    def submit(self, req_id: int, prompt_len: int, gen_len: int, group: int = -1) -> None:
+        _check(lib().zp_sched_submit(self.h, req_id, prompt_len, gen_len, group),
+               "zp_sched_submit")
+
+    def step(self) -> SchedPlan:
+        p = SchedPlanStruct()
+        _check(lib().zp_sched_step(self.h, ctypes.byref(p)), "zp_sched_step")
+        mb, nm = self.cfg.max_blocks, self.cfg.n_max
+        A, D, C = p.num_admit, p.num_decode, p.num_compress
+        return SchedPlan(
+            bool(p.restricted),
+            _arr(p.admit_id, A), _arr(p.admit_len, A), _arr(p.admit_slot, A),
+            _arr(p.admit_table, A * mb, (A, mb)), _arr(p.admit_shared, A),
+            _arr(p.new_slot, p.num_new_slots),
+            _arr(p.decode_id, D), _arr(p.decode_slot, D), _arr(p.decode_len, D),
+            _arr(p.decode_pos, D), _arr(p.decode_table, D * mb, (D, mb)),
+            _arr(p.compress_id, C), _arr(p.compress_slot, C), _arr(p.compress_len, C),
+            _arr(p.compress_pos, C), _arr(p.compress_src, C * mb, (C, mb)),
+            _arr(p.compress_dst, C * nm, (C, nm)), _arr(p.compress_pinned, C),
+            _arr(p.preempt_id, p.num_preempt))
+
+    def complete(self) -> None:
+        _check(lib().zp_sched_complete(self.h), "zp_sched_complete")
+
+    def stats(self) -> dict:
+        st = SchedStatsStruct()
+        _check(lib().zp_sched_get_stats(self.h, ctypes.byref(st)), "zp_sched_get_stats")
+        return {name: int(getattr(st, name)) for name, _ in st._fields_}
+
+    def refcount(self, block: int) -> int:
+        return int(lib().zp_bm_refcount(lib().zp_sched_block_manager(self.h), block))
+
+
 def version() -> str:
     return lib().zp_version().decode()
 
@@ -466,7 +602,7 @@ __all__: Tuple[str, ...] = (
     "alloc_workspace", "zp_compress_workspace_bytes", "zp_compress",
     "zp_update_global", "zp_workspace_error", "zp_paged_decode",
     "zp_capture_queries", "zp_paged_decode_append", "zp_decode_workspace_bytes",
-    "zp_paged_decode_split", "zp_redundancy_full",
+    "zp_paged_decode_split", "zp_redundancy_full", "Scheduler", "SchedPlan",
     "timing_enable", "timing_read", "BlockManager", "Plan", "version",
     "EXPORTED",
 )

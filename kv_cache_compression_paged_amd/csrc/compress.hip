@@ -64,6 +64,7 @@ struct ScoreArgs {
   const int32_t* src_table;
   const int32_t* dst_table;
   const int32_t* n_pinned;
+  const int32_t* seq_pos;  // ring position base (NULL: n)
   int32_t* keep;
   float* attn;
   float* red;
@@ -174,9 +175,10 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(ScoreArgs a) {
   const int S = a.n_pinned[r];
   const bool protect = (a.flags & ZP_PROTECT_WINDOW) != 0;
   const bool causal = (a.flags & ZP_NONCAUSAL) == 0;
+  const int ring_p = ((a.flags & ZP_WINDOW_RING) && a.seq_pos) ? a.seq_pos[r] : n;
   bool bad = n < a.n_max * kB || n > a.n_cap || (n + kB - 1) / kB > a.max_blocks ||
              (n + kB - 1) / kB > 1024 || slot < 0 || slot >= a.num_slots || S < 0 ||
-             S * kB + (protect ? a.w : 0) > a.k;
+             S * kB + (protect ? a.w : 0) > a.k || ring_p < a.w;
   const int nt = (n + kB - 1) / kB;
   const int32_t* src_tab = a.src_table + static_cast<int64_t>(r) * a.max_blocks;
   const int32_t* dst_tab = a.dst_table + static_cast<int64_t>(r) * a.n_max;
@@ -211,10 +213,10 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(ScoreArgs a) {
     for (int rt = 0; rt < RTW; ++rt) {
       const int row = (rt0 + rt) * 16 + nl;
       if (rt < nrt && row < a.wG) {
-        // window row i holds position n - w + i, or, in a ring, row
-        // (n - w + i) mod w does
+        // window row i is the i-th of the last w queries: row i of a
+        // linear window, ring row (P - w + i) mod w of a ring
         const int i0 = row / a.G, g = row - i0 * a.G;
-        const int i = (a.flags & ZP_WINDOW_RING) ? (n - a.w + i0) % a.w : i0;
+        const int i = (a.flags & ZP_WINDOW_RING) ? (ring_p - a.w + i0) % a.w : i0;
         q[rt].load(qbase + (static_cast<int64_t>(i) * a.Hq + h * a.G + g) * D * E::kBytes +
                    jg * (D / 4) * E::kBytes);
       } else {
@@ -791,6 +793,7 @@ zp_status launch_compress(const CompressGeom& g, const zp_kv_pool& pool,
   a.src_table = batch.src_table;
   a.dst_table = batch.dst_table;
   a.n_pinned = batch.n_pinned;
+  a.seq_pos = batch.seq_pos;
   a.keep = out.keep_idx;
   a.attn = out.attn;
   a.red = out.red;

@@ -50,18 +50,21 @@ def test_capture_matches_oracle_over_decode_steps(dtype, d):
     _say(f"[capture] {dtype} d={d}: {2 * w + 3} steps bit-exact")
 
 
-def _linear_to_ring(q_window, n_tok, slots, w):
-    """Ring layout of a linear window: position n-w+i goes to row (n-w+i) mod w."""
+def _linear_to_ring(q_window, seq, slots, w):
+    """Ring layout of a linear window: the query of sequence position
+    P-w+i (P = seq[r], the next token's position) goes to row (P-w+i) mod w."""
     ring = torch.empty_like(q_window)
     for r, s in enumerate(slots):
-        n = int(n_tok[r])
-        idx = torch.tensor([(n - w + i) % w for i in range(w)], device=q_window.device)
+        P = int(seq[r])
+        idx = torch.tensor([(P - w + i) % w for i in range(w)], device=q_window.device)
         ring[s, :, idx] = q_window[s]
     return ring
 
 
-@pytest.mark.parametrize("flags", [0, Z.ZP_NONCAUSAL])
-def test_ring_window_compression_is_bit_identical(flags):
+@pytest.mark.parametrize("flags,shift", [(0, 0), (Z.ZP_NONCAUSAL, 0), (0, 16), (0, 37)])
+def test_ring_window_compression_is_bit_identical(flags, shift):
+    """shift > 0: the sequence is ahead of the cache (earlier compressions
+    evicted tokens), so the ring is indexed by seq_pos, not n."""
     spec = synth.scaled(synth.EIGHT_B, requests=3, layers=2, kv_heads=2, q_heads=8,
                         n_max=20, pool_blocks=3 * 20 + 3 * 3)
     n = spec.n_tokens
@@ -71,15 +74,22 @@ def test_ring_window_compression_is_bit_identical(flags):
     rparams, _ = P._params_for(spec, flags | Z.ZP_WINDOW_RING)
     R, L, H = spec.requests, spec.layers, spec.kv_heads
     U, k = R * L * H, spec.keep
-    ring = _linear_to_ring(wl.q_window, n_tok, wl.slots, spec.window)
+    seq = np.asarray(n_tok) + shift
+    ring = _linear_to_ring(wl.q_window, seq, wl.slots, spec.window)
+    ring_batch = Z.DeviceBatch(slot=dev.slot, n_tokens=dev.n_tokens,
+                               src_table=dev.src_table, dst_table=dev.dst_table,
+                               n_pinned=dev.n_pinned, num_slots=dev.num_slots,
+                               n_cap=dev.n_cap,
+                               seq_pos=(torch.from_numpy(seq.astype(np.int32)).cuda()
+                                        if shift else None))
     results = []
-    for qw, prm in ((wl.q_window, zparams), (ring, rparams)):
+    for qw, prm, bt in ((wl.q_window, zparams, dev), (ring, rparams, ring_batch)):
         kp, vp, g = wl.k_pool.clone(), wl.v_pool.clone(), glob.clone()
         pool = Z.make_pool(kp, vp)
         out = Z.alloc_outputs(U, k, dev.n_cap, "cuda", debug=True)
         ws = Z.alloc_workspace(pool, prm, R, "cuda")
-        Z.zp_compress(pool, dev, qw, g, prm, out, ws)
-        Z.zp_update_global(g, pool, dev, out, prm)
+        Z.zp_compress(pool, bt, qw, g, prm, out, ws)
+        Z.zp_update_global(g, pool, bt, out, prm)
         torch.cuda.synchronize()
         assert Z.zp_workspace_error(ws) == Z.ZP_OK
         results.append((kp, vp, g, out))
