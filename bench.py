@@ -24,7 +24,9 @@ With --workload capture_8b_32L_32q it times query-window capture alone (128
 slot-holding requests x 32 layers x 32 query heads of 128, w = 32); with
 --workload decode_8b_32L_8kv_32q the decode consumer (plain, with append, and
 split-K on a long-context small batch); with --workload redundancy_ablation_8b
-the all-pairs redundancy against the whole compression step on 1024 units.
+the all-pairs redundancy against the whole compression step on 1024 units;
+with --workload engine_8b the model-free engine loop (scheduler, capture,
+compression beside decode) at the 8B-like layout.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        [--cpu-seconds S] [--no-cpu]
@@ -498,6 +500,62 @@ def run_redundancy_ablation(args):
     }), flush=True)
 
 
+def run_engine(args):
+    """The engine loop at the 8B-like layout (32 layers, 8 KV heads, 32 query
+    heads of 128, b = 16, N_max = 256, w = 32): 96 running requests, each
+    holding one of 96 query slots, prompts U[3800, 4064) tokens (just under
+    the slot threshold) and generations U[200, 1200): after the warm-up every
+    request compresses each time it fills its tail block, beside the decode of
+    the others. Random K/V rows and queries stand in for a model. Timed over
+    K steps after W warm-up steps; reports decode tokens/s, compressed tokens/s
+    and the time of each stream."""
+    import torch
+    from kv_cache_compression_paged_amd.sim import Engine, EngineConfig
+    cfg = EngineConfig(layers=32, kv_heads=8, q_heads=32, head_dim=128, block_size=16,
+                       n_max=256, window=32, num_blocks=96 * 256 + 2048, query_slots=96,
+                       max_running=96, max_blocks=340, seed=2024,
+                       prefill_bank_blocks=320)
+    eng = Engine(cfg)
+    rng = np.random.default_rng(7)
+    nreq = 2048
+    for rid in range(nreq):
+        eng.submit(rid, int(rng.integers(3800, 4064)), int(rng.integers(200, 1200)))
+    warm, steps = max(args.warmup, 1) * 150, max(args.steps, 1) * 12
+    t_w = time.perf_counter()
+    for i in range(warm):
+        eng.step()
+        if i % 50 == 49:
+            print(f"[bench] engine warm-up step {i + 1}: {eng.sched.stats()}",
+                  file=sys.stderr, flush=True)
+    print(f"[bench] engine warm-up {warm} steps in {time.perf_counter() - t_w:.1f} s",
+          file=sys.stderr, flush=True)
+    s0 = eng.sched.stats()
+    for key in eng.time:
+        eng.time[key] = 0.0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        eng.step()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    s1 = eng.sched.stats()
+    d = {k: s1[k] - s0[k] for k in ("tokens", "compressions", "preemptions",
+                                   "restricted_steps", "admitted", "finished")}
+    print(json.dumps({
+        "metric": "engine loop: decode tokens/s with compression beside decoding",
+        "value": round(d["tokens"] / el, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": steps, "warmup": warm, "ms_per_step": round(el * 1e3 / steps, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "engine_8b_96run_96slots", "layers": 32, "kv_heads": 8,
+                   "q_heads": 32, "head_dim": 128, "n_max": 256, "window": 32,
+                   "query_slots": 96, "max_running": 96},
+        "per_step": {k: round(v / steps, 3) for k, v in d.items()},
+        "stream_ms_per_step": {k: round(v / steps, 3) for k, v in eng.time.items()},
+        "compressed_tokens_per_s": round(d["compressions"] * 4096 / el, 1),
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -520,6 +578,9 @@ def main():
         return
     if args.workload == "redundancy_ablation_8b":
         run_redundancy_ablation(args)
+        return
+    if args.workload == "engine_8b":
+        run_engine(args)
         return
     spec = synth.SPECS[args.workload]
     if spec.compress_groups > 1:

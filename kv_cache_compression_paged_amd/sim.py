@@ -51,6 +51,9 @@ class EngineConfig:
     max_running: int
     max_blocks: int
     seed: int = 0
+    # > 0: prefill copies rows from a bank of this many random blocks per
+    # layer (fast set-up for long runs) instead of drawing every row
+    prefill_bank_blocks: int = 0
 
 
 @dataclass
@@ -89,6 +92,12 @@ class Engine:
         self.gen.manual_seed(c.seed)
         self.sc, self.sd = torch.cuda.Stream(), torch.cuda.Stream()
         self.records: List[StepRecord] = []
+        self.bank = None
+        if c.prefill_bank_blocks > 0:
+            self.bank = (self._randn((c.layers, c.prefill_bank_blocks, c.kv_heads,
+                                      c.block_size, c.head_dim)),
+                         self._randn((c.layers, c.prefill_bank_blocks, c.kv_heads,
+                                      c.block_size, c.head_dim)))
         self.prefixes: List[np.ndarray] = []
         self.time = dict(compress_ms=0.0, decode_ms=0.0, step_ms=0.0)
 
@@ -133,7 +142,13 @@ class Engine:
             first = shared // c.block_size
             ids = plan.admit_table[i, first:nb].astype(np.int64)
             shape = (c.layers, nb - first, c.kv_heads, c.block_size, c.head_dim)
-            k, v = self._randn(shape), self._randn(shape)
+            if self.bank is not None and nb - first <= c.prefill_bank_blocks:
+                off = int(t.randint(0, c.prefill_bank_blocks - (nb - first) + 1, (1,),
+                                    generator=self.gen, device=self.dev).item())
+                k = self.bank[0][:, off:off + nb - first]
+                v = self.bank[1][:, off:off + nb - first]
+            else:
+                k, v = self._randn(shape), self._randn(shape)
             idx = t.from_numpy(ids).to(self.dev)
             self.k_pool[:, idx] = k
             self.v_pool[:, idx] = v
