@@ -94,12 +94,15 @@ def build_inputs(case: Case, device: str = "cuda"):
         free = [x for x in range(spec.pool_blocks) if x not in used]
         extra_pool = free
     nxt = 0
+    refc = wl.refcount.copy()
     for r in range(R):
         tables[r, :spec.n_max] = base[r]
         nb = (int(n_tok[r]) + b - 1) // b
         for j in range(spec.n_max, nb):
             tables[r, j] = extra_pool[nxt]
+            refc[extra_pool[nxt]] += 1        # held by the request from now on
             nxt += 1
+    wl.refcount = refc
     if case.identical_keys:
         wl.k_pool[:] = wl.k_pool[0, 0, 0, 0].clone()
     if case.outlier is not None:
@@ -118,7 +121,6 @@ def build_inputs(case: Case, device: str = "cuda"):
         glob = torch.from_numpy(np.ascontiguousarray(
             case.global_override.astype(np.float32))).to(device)
     # plan: block manager of the library (checked against the oracle's)
-    refc = wl.refcount
     bm_plan = None
     if case.use_block_manager:
         bm = Z.BlockManager(spec.pool_blocks)

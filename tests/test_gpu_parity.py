@@ -494,3 +494,33 @@ def test_full_size_overlap_sampled():
          f"match the oracle over their kept tokens")
     del wl, out, dec, dec1
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------- edge shapes ---
+
+EDGE_CASES = [
+    # N_max = 2: one kept block, k = b
+    ("n_max 2", P.Case(synth.scaled(EIGHT_B, requests=2, n_max=2, window=8,
+                                    pool_blocks=8))),
+    # G = 1 (no grouping) and a window as long as the kept part
+    ("G 1, w = k", P.Case(synth.scaled(EIGHT_B, requests=2, kv_heads=2, q_heads=2,
+                                       n_max=6, window=80, pool_blocks=16))),
+    # the largest window: w*G = 192 rows with head_dim 64
+    ("d64, 192 window rows", P.Case(synth.scaled(D64, q_heads=12, window=32,
+                                                 n_max=20, pool_blocks=48))),
+    # fp32 keys with head_dim 128 at the largest row count it supports (64)
+    ("fp32 d128, 64 rows", P.Case(synth.scaled(F32_D128, q_heads=4, window=16))),
+    # a shared prefix together with the protected window
+    ("prefix + protected window", P.Case(PREFIX, flags=Z.ZP_PROTECT_WINDOW,
+                                         use_block_manager=True)),
+    # prefill overshoot on requests that share a prefix (freed tail blocks)
+    ("prefix + overshoot", P.Case(
+        synth.scaled(PREFIX, pool_blocks=PREFIX.pool_blocks + 16),
+        n_tokens=[PREFIX.n_tokens + e for e in (3, 16, 17, 40)],
+        max_blocks=PREFIX.n_max + 3, use_block_manager=True)),
+]
+
+
+@pytest.mark.parametrize("label,case", EDGE_CASES, ids=[c[0] for c in EDGE_CASES])
+def test_edge_shapes(label, case):
+    _check(case, label)
