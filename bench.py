@@ -1,7 +1,8 @@
 """Throughput of the Compressed-PagedAttention compression step on one GPU.
 
 A step is one whole compression pass over the batch: zp_compress (score,
-select and K/V compaction in one kernel) followed by zp_update_global, for every
+select, K/V compaction and, with ZP_UPDATE_GLOBAL, the global-score update in
+one kernel; --separate-update runs zp_update_global as its own launch), for every
 (request, layer, KV head) unit of the workload. The default workload is the
 8B-like shape: 128 requests x 32 layers x 8 KV heads (32 query heads),
 head_dim 128, b = 16, N_max = 256 (4096 tokens, keep 4080), w = 32, bf16
@@ -58,6 +59,8 @@ def parse():
     ap.add_argument("--workload", default="8b_32L_8kv_32q_N4096")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--separate-update", action="store_true",
+                    help="run the global-score update as its own launch")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 1 GiB device copy first (counter scaling)")
     return ap.parse_args()
@@ -597,7 +600,10 @@ def main():
     U = R * L * H
     k, n = spec.keep, spec.n_tokens
     dt = Z.ZP_BF16 if spec.dtype == "bf16" else Z.ZP_F32
-    params = Z.make_params(spec.n_max, spec.window, spec.q_heads, dt)
+    # the step's global-score update runs inside the compression kernel
+    # (ZP_UPDATE_GLOBAL: the same update zp_update_global applies)
+    params = Z.make_params(spec.n_max, spec.window, spec.q_heads, dt,
+                           flags=0 if args.separate_update else Z.ZP_UPDATE_GLOBAL)
     pool = Z.make_pool(wl.k_pool, wl.v_pool)
     tables = torch.from_numpy(wl.tables).to(dev)
     batch = Z.DeviceBatch(
@@ -645,7 +651,8 @@ def main():
         out.first_hole = holes[i]
         Z.zp_compress(pool, batch, wl.q_window, globs[i], params, out, ws,
                       stream)
-        Z.zp_update_global(globs[i], pool, batch, out, params, stream)
+        if args.separate_update:
+            Z.zp_update_global(globs[i], pool, batch, out, params, stream)
 
     for i in range(warm):
         step(i)
@@ -669,6 +676,9 @@ def main():
     hole_np = holes[warm:].cpu().numpy().astype(np.int64)
     M = (k - hole_np).clip(min=0)                      # moved rows per unit
     per_step = [unit_bytes(spec, M[i]) for i in range(steps)]
+    if not args.separate_update:   # the update's bytes are the compression kernel's
+        for p in per_step:
+            p["compress"] += p.pop("global_update")
     alg = {key: float(np.mean([p[key] for p in per_step])) for key in per_step[0]}
     ms_step = elapsed * 1e3 / steps
     tokens_step = float(np.sum(wl.n_tokens))

@@ -57,6 +57,10 @@ typedef int32_t zp_status;
 #define ZP_WINDOW_RING    (1u << 2) /* q_window rows form a ring: the query of
                                        position p sits in row p mod w (the
                                        layout zp_capture_queries writes)     */
+#define ZP_UPDATE_GLOBAL  (1u << 3) /* zp_compress also applies the global-
+                                       score update of zp_update_global in
+                                       the same kernel (then that call must
+                                       not follow for this batch)            */
 
 /* A paged KV pool: k and v are device arrays laid out
  * [layers][num_blocks][kv_heads][block_size][head_dim] of `dtype`, 16-byte
@@ -87,7 +91,8 @@ typedef struct {
  *               - w_red*red (the pages name the three parts, [zh] §2.1,
  *               without a formula; 1, 0.5, 0.5 is the documented default).
  *   sm_scale -- softmax scale; <= 0 selects 1/sqrt(head_dim).
- *   flags    -- ZP_NONCAUSAL, ZP_PROTECT_WINDOW, ZP_WINDOW_RING. */
+ *   flags    -- ZP_NONCAUSAL, ZP_PROTECT_WINDOW, ZP_WINDOW_RING,
+ *               ZP_UPDATE_GLOBAL. */
 typedef struct {
   int32_t  n_max;
   int32_t  window;
@@ -175,15 +180,16 @@ zp_status zp_compress_workspace_bytes(const zp_kv_pool* pool,
  *      otherwise; shared blocks are never written ([zh] §2.2).
  * q_window: device [num_slots][layers][w][q_heads][head_dim] of q_dtype.
  * global_scores: device [num_slots][layers][kv_heads][n_cap] fp32 (read only
- * here; see zp_update_global). workspace: device, 256-byte aligned, at least
+ * here unless ZP_UPDATE_GLOBAL is set, then updated in place as by
+ * zp_update_global). workspace: device, 256-byte aligned, at least
  * zp_compress_workspace_bytes; it also receives the device error word.
  * Errors: ZP_EINVAL, ZP_EUNSUPPORTED (head_dim not 64/128, block_size not 16,
  * w*G > 192 -- 64 for fp32 with head_dim 128 --, n_cap > 16384, or, for fp32
- * with head_dim 128 only, n_cap above about 6700: the per-token scores of a
+ * with head_dim 128 only, n_cap above about 6100: the per-token scores of a
  * unit live in on-chip memory beside the key ring), ZP_EWORKSPACE, ZP_EHIP.
  * Nothing is written when an error is returned. */
 zp_status zp_compress(const zp_kv_pool* pool, const zp_batch* batch,
-                      const void* q_window, const float* global_scores,
+                      const void* q_window, float* global_scores,
                       const zp_params* params, const zp_compress_out* out,
                       void* workspace, size_t workspace_bytes, void* stream);
 

@@ -36,6 +36,7 @@ ZP_BF16 = 1
 ZP_NONCAUSAL = 1 << 0
 ZP_PROTECT_WINDOW = 1 << 1
 ZP_WINDOW_RING = 1 << 2
+ZP_UPDATE_GLOBAL = 1 << 3
 
 ZP_KERNEL_COMPRESS = 0
 ZP_KERNEL_GLOBAL = 1

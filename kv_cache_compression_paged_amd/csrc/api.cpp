@@ -123,7 +123,7 @@ zp_status make_geom(const zp_kv_pool* pool, const zp_params* p,
   if (!std::isfinite(p->w_attn) || !std::isfinite(p->w_global) ||
       !std::isfinite(p->w_red) || !std::isfinite(p->sm_scale))
     return fail(ZP_EINVAL, "score weights and scale must be finite");
-  if (p->flags & ~(ZP_NONCAUSAL | ZP_PROTECT_WINDOW | ZP_WINDOW_RING))
+  if (p->flags & ~(ZP_NONCAUSAL | ZP_PROTECT_WINDOW | ZP_WINDOW_RING | ZP_UPDATE_GLOBAL))
     return fail(ZP_EINVAL, "unknown flags 0x%x", p->flags);
   const int k = (p->n_max - 1) * pool->block_size;
   if ((p->flags & ZP_PROTECT_WINDOW) && p->window > k)
@@ -193,7 +193,7 @@ zp_status zp_compress_workspace_bytes(const zp_kv_pool* pool,
 }
 
 zp_status zp_compress(const zp_kv_pool* pool, const zp_batch* batch,
-                      const void* q_window, const float* global_scores,
+                      const void* q_window, float* global_scores,
                       const zp_params* params, const zp_compress_out* out,
                       void* workspace, size_t workspace_bytes, void* stream) {
   CompressGeom g;

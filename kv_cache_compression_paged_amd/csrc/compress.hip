@@ -58,7 +58,7 @@ struct ScoreArgs {
   void* kpool;
   void* vpool;
   const void* q_window;
-  const float* glob;
+  float* glob;
   const int32_t* slot;
   const int32_t* n_tokens;
   const int32_t* src_table;
@@ -147,13 +147,13 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(ScoreArgs a) {
   __shared__ float xchg[kQuarters][4][16];
   __shared__ int scratch[16];
   __shared__ int sel[2];
-  // The ring is idle between sweeps (each ends with all loads landed and a
-  // barrier) and during the select: the per-quarter row statistics and the
-  // per-wave histograms live in it then.
-  static_assert(2 * kQuarters * kRows * 4 <= sizeof(ring) &&
-                kWaves * 257 * 4 <= sizeof(ring), "ring too small to alias");
-  float (*st_m)[kRows] = reinterpret_cast<float (*)[kRows]>(&ring[0][0][0]);
-  float (*st_z)[kRows] = reinterpret_cast<float (*)[kRows]>(&ring[0][0][0] + kQuarters * kRows * 4);
+  __shared__ float st_m[kQuarters][kRows];  // per-quarter row statistics
+  __shared__ float st_z[kQuarters][kRows];
+  // The ring is idle during the select (the column sweep ended with all
+  // loads landed and a barrier): the per-wave histograms live in it then.
+  // (Between the sweeps it is not idle: the column sweep starts on the
+  // blocks the first sweep left there.)
+  static_assert(kWaves * 257 * 4 <= sizeof(ring), "ring too small to alias");
   uint32_t (*hist)[257] = reinterpret_cast<uint32_t (*)[257]>(&ring[0][0][0]);  // one per wave
 
   const int tid = threadIdx.x;
@@ -297,14 +297,27 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(ScoreArgs a) {
     }
     step_barrier();
   };
+  // The block of forward step p sits in slot p mod kRing. A forward sweep
+  // leaves the blocks of its last kRing steps in the ring; the backward
+  // sweep that follows starts with exactly those blocks (its step s is
+  // forward step last - s), so it reads them in place and loads only from
+  // its step kRing on. The waits stay exact: every step it does load comes
+  // after every step it does not.
+  // Slots are walked with counters: up from 0 forward, down from
+  // last mod kRing backward.
+  auto needs_load = [&](int s) { return s <= last && !(backward && s < kRing); };
   auto sweep = [&](auto&& mma, auto&& valu, auto&& after) {
     static_assert(kRing >= 4, "double steps need four ring slots");
-    int slot_w = 0;
+    const int base = backward && last >= 0 ? last % kRing : 0;
+    auto adv = [&](int slot) {
+      return backward ? (slot == 0 ? kRing - 1 : slot - 1) : (slot + 1 == kRing ? 0 : slot + 1);
+    };
+    int slot_w = base;
     for (int p = 0; p < kRing - 2; ++p) {
-      if (p <= last) issue(p, slot_w);
-      slot_w = slot_w + 1 == kRing ? 0 : slot_w + 1;
+      if (needs_load(p)) issue(p, slot_w);
+      slot_w = adv(slot_w);
     }
-    int slot_r = 0;
+    int slot_r = base;
     const int niters = (nsteps + 1) / 2;
     for (int i = 0; i < niters; ++i) {
       const int sa = 2 * i, sb = 2 * i + 1;
@@ -312,10 +325,10 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(ScoreArgs a) {
       after(i);
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        if (sa + kRing - 2 + e <= last) issue(sa + kRing - 2 + e, slot_w);
-        slot_w = slot_w + 1 == kRing ? 0 : slot_w + 1;
+        if (needs_load(sa + kRing - 2 + e)) issue(sa + kRing - 2 + e, slot_w);
+        slot_w = adv(slot_w);
       }
-      const int slot_b = slot_r + 1 == kRing ? 0 : slot_r + 1;
+      const int slot_b = adv(slot_r);
       Acc acc_a, acc_b;
       if (sa <= last) {
         FragT kc;
@@ -329,7 +342,7 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(ScoreArgs a) {
       }
       if (sa <= last) valu(acc_a, tile_of(sa), sa);
       if (sb <= last) valu(acc_b, tile_of(sb), sb);
-      slot_r = slot_b + 1 == kRing ? 0 : slot_b + 1;
+      slot_r = adv(slot_b);
     }
     wait_vm_lgkm0(0);
     step_barrier();
@@ -498,7 +511,7 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(ScoreArgs a) {
       mp[rt][i] = rt < nrt ? mprime[(rt0 + rt) * 16 + jg * 4 + i] : INFINITY;
   const float inv_rows = 1.f / static_cast<float>(a.wG);
   const int64_t urow = static_cast<int64_t>(u) * a.n_cap;
-  const float* grow = a.glob + (static_cast<int64_t>(slot * a.L + l) * a.Hkv + h) * a.n_cap;
+  float* grow = a.glob + (static_cast<int64_t>(slot * a.L + l) * a.Hkv + h) * a.n_cap;
   const int pin_lo = S * kB;
   const int pin_hi = protect ? n - a.w : n;
   float cs_prev[2] = {0.f, 0.f};
@@ -659,6 +672,35 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(ScoreArgs a) {
       }
   }
   if (tid == 0 && a.hole_out) a.hole_out[u] = hole;
+  __syncthreads();  // keep_l complete
+
+  // ---- optional global-score update, as zp_update_global does it: the
+  // row follows its tokens, g'_t = g_{keep[t]} + attn_{keep[t]} for t < k,
+  // 0 after. In place, in ascending chunks: a chunk's values are all read
+  // before any of them is written, and a later chunk reads only at or above
+  // its own start (keep[t] >= t), never what an earlier chunk wrote.
+  if (a.flags & ZP_UPDATE_GLOBAL) {
+    constexpr int kPer = 4;
+    for (int c0 = 0; c0 < a.n_cap; c0 += kPer * kThreads) {
+      float gv[kPer];
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int t = c0 + j * kThreads + tid;
+        float v = 0.f;
+        if (t < a.k) {
+          const int sp = keep_l[t];
+          v = grow[sp] + a.attn[urow + sp];
+        }
+        gv[j] = v;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int t = c0 + j * kThreads + tid;
+        if (t < a.n_cap) grow[t] = gv[j];
+      }
+    }
+  }
 
   // ---- compaction: kept K and V rows, in order, to logical rows [0, k)
   // ([zh] §2.1 re-packing into the first N_max-1 blocks; [zh] §2.2 target
@@ -781,7 +823,7 @@ namespace zp {
 
 zp_status launch_compress(const CompressGeom& g, const zp_kv_pool& pool,
                           const zp_batch& batch, const void* q_window,
-                          const float* global_scores,
+                          float* global_scores,
                           const zp_compress_out& out, int32_t* err, void* stream) {
   ScoreArgs a;
   a.kpool = pool.k;

@@ -28,7 +28,7 @@ struct CompressGeom {
 // (launch error), after recording the error text.
 zp_status launch_compress(const CompressGeom& g, const zp_kv_pool& pool,
                           const zp_batch& batch, const void* q_window,
-                          const float* global_scores,
+                          float* global_scores,
                           const zp_compress_out& out, int32_t* err, void* stream);
 zp_status launch_global(const CompressGeom& g, float* global_scores,
                         const zp_batch& batch, const int32_t* keep,

@@ -179,7 +179,7 @@ def _compress(pool=None, batch=None, params=None, ws_bytes=1 << 20,
     (dict(params=_params(q_dtype=Z.ZP_F32)), Z.ZP_EUNSUPPORTED),
     (dict(params=_params(n_max=1)), Z.ZP_EINVAL),
     (dict(params=_params(window=0)), Z.ZP_EINVAL),
-    (dict(params=_params(flags=8)), Z.ZP_EINVAL),
+    (dict(params=_params(flags=1 << 7)), Z.ZP_EINVAL),
     (dict(params=_params(window=49, flags=Z.ZP_PROTECT_WINDOW)), Z.ZP_EINVAL),
     (dict(params=_params(w_red=float("nan"))), Z.ZP_EINVAL),
     (dict(params=_params(window=64, q_heads=8)), Z.ZP_EUNSUPPORTED),  # w*G=256

@@ -524,3 +524,45 @@ EDGE_CASES = [
 @pytest.mark.parametrize("label,case", EDGE_CASES, ids=[c[0] for c in EDGE_CASES])
 def test_edge_shapes(label, case):
     _check(case, label)
+
+
+@pytest.mark.parametrize("label,case", [
+    ("in place", P.Case(EIGHT_B)),
+    ("overshoot", P.Case(synth.scaled(EIGHT_B, requests=3, pool_blocks=112 + 12),
+                         n_tokens=[EIGHT_B.n_tokens + e for e in (5, 16, 37)],
+                         max_blocks=EIGHT_B.n_max + 3)),
+    ("shared prefix", P.Case(PREFIX, use_block_manager=True)),
+], ids=["in place", "overshoot", "shared prefix"])
+def test_fused_global_update_is_bit_identical(label, case):
+    """ZP_UPDATE_GLOBAL applies the global-score update inside the
+    compression kernel: pools, keep sets, attention and the updated global
+    scores must equal those of zp_compress followed by zp_update_global, bit
+    for bit (the update is the same single fp32 addition)."""
+    spec = case.spec
+    wl, glob, host, dev, tables, dst, pinned, n_tok, _ = P.build_inputs(case)
+    R, L, H = spec.requests, spec.layers, spec.kv_heads
+    U, k = R * L * H, spec.keep
+    zparams, _ = P._params_for(spec, 0)
+    fparams, _ = P._params_for(spec, Z.ZP_UPDATE_GLOBAL)
+    res = []
+    for fused in (False, True):
+        kp, vp, g = wl.k_pool.clone(), wl.v_pool.clone(), glob.clone()
+        pool = Z.make_pool(kp, vp)
+        out = Z.alloc_outputs(U, k, dev.n_cap, "cuda")
+        ws = Z.alloc_workspace(pool, zparams, R, "cuda")
+        if fused:
+            Z.zp_compress(pool, dev, wl.q_window, g, fparams, out, ws)
+        else:
+            Z.zp_compress(pool, dev, wl.q_window, g, zparams, out, ws)
+            Z.zp_update_global(g, pool, dev, out, zparams)
+        torch.cuda.synchronize()
+        assert Z.zp_workspace_error(ws) == Z.ZP_OK
+        res.append((kp, vp, g, out))
+    (k1, v1, g1, o1), (k2, v2, g2, o2) = res
+    assert torch.equal(k1, k2) and torch.equal(v1, v2)
+    assert torch.equal(g1.view(torch.int32), g2.view(torch.int32))
+    assert torch.equal(o1.keep_idx, o2.keep_idx)
+    for u in range(U):
+        nu = int(n_tok[u // (L * H)])
+        assert torch.equal(o1.attn[u, :nu].view(torch.int32), o2.attn[u, :nu].view(torch.int32))
+    _say(f"[parity] fused global update ({label}): bit-identical")
