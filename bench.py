@@ -606,11 +606,28 @@ def main():
                            flags=0 if args.separate_update else Z.ZP_UPDATE_GLOBAL)
     pool = Z.make_pool(wl.k_pool, wl.v_pool)
     tables = torch.from_numpy(wl.tables).to(dev)
+    if spec.shared_blocks:
+        # shared prefixes: the library's block manager plans the targets once;
+        # sources are never written in this mode, so every step repeats the
+        # same compression into the same targets
+        bm = Z.BlockManager(spec.pool_blocks)
+        bm.alloc(spec.pool_blocks)
+        for bid in range(spec.pool_blocks):
+            c = int(wl.refcount[bid])
+            if c == 0:
+                bm.release([bid])
+            for _ in range(c - 1):
+                bm.incref(bid)
+        plan = bm.plan_compress(wl.tables, wl.n_tokens, spec.n_max, spec.block_size)
+        dst_table = torch.from_numpy(np.ascontiguousarray(plan.dst_tables, dtype=np.int32)).to(dev)
+        n_pinned = torch.from_numpy(np.ascontiguousarray(plan.n_pinned, dtype=np.int32)).to(dev)
+    else:
+        dst_table = tables.clone()
+        n_pinned = torch.zeros(R, dtype=torch.int32, device=dev)
     batch = Z.DeviceBatch(
         slot=torch.from_numpy(wl.slots).to(dev),
         n_tokens=torch.from_numpy(wl.n_tokens).to(dev),
-        src_table=tables, dst_table=tables.clone(),
-        n_pinned=torch.zeros(R, dtype=torch.int32, device=dev),
+        src_table=tables, dst_table=dst_table, n_pinned=n_pinned,
         num_slots=R, n_cap=wl.n_cap)
     out = Z.alloc_outputs(U, k, wl.n_cap, dev)
     ws = Z.alloc_workspace(pool, params, R, dev)
@@ -675,6 +692,9 @@ def main():
 
     hole_np = holes[warm:].cpu().numpy().astype(np.int64)
     M = (k - hole_np).clip(min=0)                      # moved rows per unit
+    if spec.shared_blocks:   # rows [S*b, k) go to the targets
+        pin = np.repeat(batch.n_pinned.cpu().numpy().astype(np.int64), L * H)
+        M = np.broadcast_to(k - pin * spec.block_size, hole_np.shape).copy()
     per_step = [unit_bytes(spec, M[i]) for i in range(steps)]
     if not args.separate_update:   # the update's bytes are the compression kernel's
         for p in per_step:
