@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--workload", default="8b_32L_8kv_32q_N4096")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--variant", choices=("causal", "noncausal", "protect"),
+                    default="causal", help="window mask / protection variant")
     ap.add_argument("--separate-update", action="store_true",
                     help="run the global-score update as its own launch")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -602,8 +604,10 @@ def main():
     dt = Z.ZP_BF16 if spec.dtype == "bf16" else Z.ZP_F32
     # the step's global-score update runs inside the compression kernel
     # (ZP_UPDATE_GLOBAL: the same update zp_update_global applies)
+    vflags = {"causal": 0, "noncausal": Z.ZP_NONCAUSAL,
+              "protect": Z.ZP_PROTECT_WINDOW}[args.variant]
     params = Z.make_params(spec.n_max, spec.window, spec.q_heads, dt,
-                           flags=0 if args.separate_update else Z.ZP_UPDATE_GLOBAL)
+                           flags=vflags | (0 if args.separate_update else Z.ZP_UPDATE_GLOBAL))
     pool = Z.make_pool(wl.k_pool, wl.v_pool)
     tables = torch.from_numpy(wl.tables).to(dev)
     if spec.shared_blocks:
@@ -743,7 +747,7 @@ def main():
                    "head_dim": spec.head_dim, "block_size": spec.block_size,
                    "n_max": spec.n_max, "tokens_per_request": n,
                    "keep": k, "window": spec.window, "units": U,
-                   "parallelism": "single GPU"},
+                   "variant": args.variant, "parallelism": "single GPU"},
         "achieved_GBps": round(gbps, 1),
         "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
         "moved_rows_mean": round(float(M.mean()), 1),

@@ -15,6 +15,8 @@
 //            an exact radix select on order-preserving 32-bit score keys,
 //            ties broken toward the lower position, then the kept positions
 //            are written ascending together with the first evicted one;
+//   update   (with ZP_UPDATE_GLOBAL) the unit's global-score row follows
+//            its tokens: g'_t = g_{keep[t]} + attn_{keep[t]}, 0 past k;
 //   compact  move the kept K and V rows, in order, to logical rows [0, k)
 //            through the destination table ([zh] §2.1, §2.2).
 // Compaction runs in the same workgroup right after its select, so while
@@ -36,7 +38,8 @@
 // load in flight). Two waves share a SIMD, so one's MFMA overlaps the
 // other's exp/VALU work. Long contexts (token rows that do not fit beside
 // the default ring in LDS) take a 4-slot ring. The column sweep runs
-// backward so it starts on the blocks the first sweep read last.
+// backward: it starts on the blocks the first sweep read last and takes the
+// ones still in the ring without reloading them.
 #include <hip/hip_runtime.h>
 
 #include "zp_device.h"
@@ -230,8 +233,8 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(ScoreArgs a) {
   const float sl2 = a.sl2;
   const int nsteps = (nt + kQuarters - 1) / kQuarters;
   // Sweeps run forward or backward over a quarter's blocks; the backward
-  // column sweep starts with the blocks the row-statistics sweep read last,
-  // while they may still sit in the caches.
+  // column sweep starts with the blocks the row-statistics sweep read last
+  // (the newest of them are still in the ring).
   bool backward = false;
   int last_q = 0;  // last step with a block for this quarter (set below)
   auto tile_of = [&](int s) { return (backward ? last_q - s : s) * kQuarters + kq; };
