@@ -731,27 +731,53 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(ScoreArgs a) {
                (static_cast<int64_t>(l) * a.NB * a.Hkv + h) * TG::kTileBytes;
   const int piece16 = (tid % kPieces) * 16, prow = tid / kPieces;
   const int k = a.k;
-  for (int c0 = start; c0 < k; c0 += kRowsPerChunk) {
+  struct Buf {
     zpd::u32x4_t vk[kPasses], vv[kPasses];
     int64_t doff[kPasses];
-    // rows past k are clamped to row k-1 (always valid) and not stored
+  };
+  // rows past k are clamped to row k-1 (always valid) and not stored
+  auto load_chunk = [&](int c0, Buf& bf) {
 #pragma unroll
     for (int e = 0; e < kPasses; ++e) {
       const int t = min(c0 + e * kRowsPerPass + prow, k - 1);
       const int sp = keep_l[t];
       const int64_t soff = tab[sp / kB] * block_stride + (sp % kB) * TG::kRowBytes + piece16;
-      vk[e] = __builtin_nontemporal_load(reinterpret_cast<const zpd::u32x4_t*>(kmut + soff));
-      vv[e] = __builtin_nontemporal_load(reinterpret_cast<const zpd::u32x4_t*>(vmut + soff));
-      doff[e] = dtab[t / kB] * block_stride + (t % kB) * TG::kRowBytes + piece16;
+      bf.vk[e] = __builtin_nontemporal_load(reinterpret_cast<const zpd::u32x4_t*>(kmut + soff));
+      bf.vv[e] = __builtin_nontemporal_load(reinterpret_cast<const zpd::u32x4_t*>(vmut + soff));
+      bf.doff[e] = dtab[t / kB] * block_stride + (t % kB) * TG::kRowBytes + piece16;
     }
-    zpd::wait_all_memory();
-    __syncthreads();
+  };
+  auto store_chunk = [&](int c0, const Buf& bf) {
 #pragma unroll
     for (int e = 0; e < kPasses; ++e)
       if (c0 + e * kRowsPerPass + prow < k) {
-        __builtin_nontemporal_store(vk[e], reinterpret_cast<zpd::u32x4_t*>(kmut + doff[e]));
-        __builtin_nontemporal_store(vv[e], reinterpret_cast<zpd::u32x4_t*>(vmut + doff[e]));
+        __builtin_nontemporal_store(bf.vk[e], reinterpret_cast<zpd::u32x4_t*>(kmut + bf.doff[e]));
+        __builtin_nontemporal_store(bf.vv[e], reinterpret_cast<zpd::u32x4_t*>(vmut + bf.doff[e]));
       }
+  };
+  // Double buffered: the next chunk's loads go out before this chunk's are
+  // awaited (they read rows at or above the next chunk's start, which no
+  // store of this chunk touches). Loads return in order, so at most 2*kPasses
+  // outstanding memory operations means this chunk's loads have landed,
+  // whatever the order in which earlier stores complete; the raw barrier
+  // then holds every lane until all of the chunk is read.
+  auto step = [&](int c0, Buf& cur, Buf& nxt) {
+    const bool more = c0 + kRowsPerChunk < k;
+    if (more) {
+      load_chunk(c0 + kRowsPerChunk, nxt);
+      wait_vm_lgkm0(2 * kPasses);
+    } else {
+      wait_vm_lgkm0(0);
+    }
+    step_barrier();
+    store_chunk(c0, cur);
+    return more;
+  };
+  Buf b0, b1;
+  load_chunk(start, b0);
+  for (int c0 = start; c0 < k; c0 += 2 * kRowsPerChunk) {
+    if (!step(c0, b0, b1)) break;
+    if (!step(c0 + kRowsPerChunk, b1, b0)) break;
   }
 }
 
