@@ -566,3 +566,38 @@ def test_fused_global_update_is_bit_identical(label, case):
         nu = int(n_tok[u // (L * H)])
         assert torch.equal(o1.attn[u, :nu].view(torch.int32), o2.attn[u, :nu].view(torch.int32))
     _say(f"[parity] fused global update ({label}): bit-identical")
+
+
+# ------------------------------------------------- seeded random shapes ---
+
+def _random_case(seed):
+    """A small random configuration inside the supported limits."""
+    rng = np.random.default_rng(seed)
+    dtype = "bf16" if rng.random() < 0.8 else "f32"
+    d = int(rng.choice([64, 128]))
+    hkv = int(rng.integers(1, 4))
+    G = int(rng.choice([1, 2, 3, 4, 6, 8]))
+    max_rows = 64 if (dtype == "f32" and d == 128) else 192
+    n_max = int(rng.integers(2, 14))
+    w = int(rng.integers(1, min(n_max * 16, max_rows // G) + 1))
+    R = int(rng.integers(1, 4))
+    L = int(rng.integers(1, 3))
+    flags = int(rng.choice([0, Z.ZP_NONCAUSAL]))
+    if w <= (n_max - 1) * 16 and rng.random() < 0.3:
+        flags |= Z.ZP_PROTECT_WINDOW
+    over = [int(x) for x in rng.integers(0, 40, size=R)] if rng.random() < 0.4 else [0] * R
+    extra = sum((n_max * 16 + e + 15) // 16 - n_max for e in over)
+    base = synth.TINY if dtype == "f32" else synth.EIGHT_B
+    spec = synth.scaled(base, name=f"random_{seed}", seed=5000 + seed, requests=R,
+                        layers=L, kv_heads=hkv, q_heads=hkv * G, head_dim=d,
+                        n_max=n_max, window=w, pool_blocks=R * n_max + extra + 2,
+                        permute=True, near_dup=(dtype == "bf16"))
+    n = spec.n_tokens
+    return P.Case(spec, flags=flags, n_tokens=[n + e for e in over],
+                  max_blocks=n_max + 3)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_shapes(seed):
+    case = _random_case(seed)
+    _check(case, f"random shape {seed}, flags {case.flags}")
