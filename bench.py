@@ -648,7 +648,7 @@ def main():
     for _ in range(warm + steps - 1):
         globs.append(torch.rand(wl.global_scores.shape, generator=gen,
                                 device=dev, dtype=torch.float32))
-    # the box's own copy rate: a plain 2 GiB device-to-device copy
+    # the device's own copy rate: a plain 2 GiB device-to-device copy
     csrc = torch.empty(1 << 29, dtype=torch.float32, device=dev).fill_(1.0)
     cdst = torch.empty_like(csrc)
     cdst.copy_(csrc)

@@ -73,8 +73,8 @@ typedef struct {
   int32_t num_blocks;
   int32_t layers;
   int32_t kv_heads;
-  int32_t block_size;   /* b; this build supports 16                        */
-  int32_t head_dim;     /* d; this build supports 64 and 128                */
+  int32_t block_size;   /* b; the library supports 16                       */
+  int32_t head_dim;     /* d; the library supports 64 and 128               */
   int32_t dtype;        /* ZP_F32 or ZP_BF16                                */
 } zp_kv_pool;
 

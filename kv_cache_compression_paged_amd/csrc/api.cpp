@@ -93,10 +93,10 @@ zp_status check_pool(const zp_kv_pool* pool) {
   if (pool->dtype != ZP_F32 && pool->dtype != ZP_BF16)
     return fail(ZP_EINVAL, "pool dtype %d unknown", pool->dtype);
   if (pool->block_size != 16)
-    return fail(ZP_EUNSUPPORTED, "block_size %d (this build supports 16)",
+    return fail(ZP_EUNSUPPORTED, "block_size %d (the library supports 16)",
                 pool->block_size);
   if (pool->head_dim != 64 && pool->head_dim != 128)
-    return fail(ZP_EUNSUPPORTED, "head_dim %d (this build supports 64, 128)",
+    return fail(ZP_EUNSUPPORTED, "head_dim %d (the library supports 64 and 128)",
                 pool->head_dim);
   return ZP_OK;
 }

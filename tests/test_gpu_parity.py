@@ -306,8 +306,10 @@ def _sample_units(U, n_samples, seed):
     return sorted(units | {0, U - 1})
 
 
-def _full_size_sampled(spec, n_samples, seed):
-    """Run the full call and check sampled units against the oracle."""
+def _full_size_sampled(spec, n_samples, seed, fused=False):
+    """Run the full call and check sampled units against the oracle. With
+    fused=True the global update runs inside the compression kernel
+    (ZP_UPDATE_GLOBAL), the launch configuration bench.py times."""
     dev = "cuda"
     _say(f"[full] generating {spec.name}")
     wl = synth.make(spec, device=dev)
@@ -331,7 +333,7 @@ def _full_size_sampled(spec, n_samples, seed):
         dst, pinned = tables.copy(), np.zeros(R, dtype=np.int32)
     tab_dev = torch.from_numpy(tables).to(dev)
     saved = _save_units(spec, wl, tab_dev, units)
-    zparams, _ = P._params_for(spec, 0)
+    zparams, _ = P._params_for(spec, Z.ZP_UPDATE_GLOBAL if fused else 0)
     pool = Z.make_pool(wl.k_pool, wl.v_pool)
     batch = Z.DeviceBatch(
         slot=torch.from_numpy(wl.slots).to(dev),
@@ -344,7 +346,8 @@ def _full_size_sampled(spec, n_samples, seed):
     ws = Z.alloc_workspace(pool, zparams, R, dev)
     _say(f"[full] compress {spec.name}: U={U}")
     Z.zp_compress(pool, batch, wl.q_window, wl.global_scores, zparams, out, ws)
-    Z.zp_update_global(wl.global_scores, pool, batch, out, zparams)
+    if not fused:
+        Z.zp_update_global(wl.global_scores, pool, batch, out, zparams)
     torch.cuda.synchronize()
     assert Z.zp_workspace_error(ws) == Z.ZP_OK
     _check_all_units(spec, out, wl.global_scores, bool(spec.shared_blocks))
@@ -359,7 +362,8 @@ def test_full_size_small_model_sampled():
 
 
 def test_full_size_8b_sampled():
-    _full_size_sampled(synth.EIGHT_B, 6, 12)
+    # the timed launch: global update inside the compression kernel
+    _full_size_sampled(synth.EIGHT_B, 6, 12, fused=True)
 
 
 def test_full_size_prefix_sampled():

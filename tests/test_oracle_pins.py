@@ -315,7 +315,7 @@ def test_update_global_identities():
     np.testing.assert_allclose(ident[:k], g[:k] + attn[:k], rtol=1e-15)
 
 
-# ---------------------------------------------------- whole batch driver ---
+# ------------------------------------------------------------ whole batch ---
 
 def _tiny_batch(rng, R=2, L=2, H=2, G=2, d=8, b=4, n_max=4, w=3, extra=0):
     nb = R * (n_max + extra) + 3
