@@ -123,6 +123,16 @@ def traffic_from_profile(kernel: str, spec):
         return None
 
 
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(spec, wl, seconds: float) -> dict:
     """The oracle, unchanged, on a bounded seeded sample of units."""
     import oracle as O
@@ -162,7 +172,7 @@ def cpu_baseline(spec, wl, seconds: float) -> dict:
             done += 1
     tokens_per_s = done * n / (L * H) / t_cpu
     return {"value": tokens_per_s, "unit": "tokens/s", "cores": 1,
-            "kind": "oracle",
+            "kind": "oracle", "cpu": _cpu_model(), "host_cpus": os.cpu_count(),
             "sample": f"{done} seeded (request, layer, kv_head) units of this "
                       f"workload, full oracle chain (score, select, K/V "
                       f"compaction, global update), {t_cpu:.1f} s on one "
@@ -683,11 +693,15 @@ def main():
     Z.timing_read()  # drop anything recorded before
     Z.timing_enable(True)
     torch.cuda.synchronize()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
+    marks[0].record(stream)
     for i in range(warm, warm + steps):
         step(i)
+        marks[i - warm + 1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    step_ms = np.array([marks[j].elapsed_time(marks[j + 1]) for j in range(steps)])
     Z.timing_enable(False)
     kern = Z.timing_read()
     if Z.zp_workspace_error(ws) != Z.ZP_OK:
@@ -739,7 +753,9 @@ def main():
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": steps, "warmup": warm,
-        "ms_per_step": round(ms_step, 3), "higher_is_better": True,
+        "ms_per_step": round(ms_step, 3),
+        "ms_step_median": round(float(np.median(step_ms)), 3),
+        "ms_step_min": round(float(step_ms.min()), 3), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": spec.dtype,
         "data": "synthetic",
         "config": {"workload": spec.name, "requests": R, "layers": L,
