@@ -95,15 +95,17 @@ def unit_bytes(spec, M: np.ndarray) -> dict:
 KERNEL_SOURCES = {
     "compress": ["compress.hip", "zp_device.h"],
     "global_update": ["global_update.hip", "zp_device.h"],
+    "paged_decode": ["decode.hip", "zp_device.h"],
+    "capture": ["capture.hip", "zp_device.h"],
 }
 
 
-def traffic_from_profile(kernel: str, spec):
+def traffic_from_profile(kernel: str, workload: str):
     """HBM bytes per launch from the committed counter summary of `kernel` on
     this workload, or None when there is none or the kernel's sources changed
     since the counters were taken (the summary records their hash)."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"hbm_{kernel}_{spec.name}.txt")
+    path = os.path.join(ROOT, "profiles", f"hbm_{kernel}_{workload}.txt")
     if not os.path.exists(path) or kernel not in KERNEL_SOURCES:
         return None
     fields = {}
@@ -368,7 +370,8 @@ def run_capture(args):
                    "q_heads": Hq, "head_dim": d, "window": w},
         "roofline": {"bound": "hbm", "kernel": "capture", "achieved": round(ach, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(ach / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic_from_profile("capture", "capture_8b_32L_32q"),
                      "alg_bytes_per_launch": round(nbytes)},
     }), flush=True)
 
@@ -446,7 +449,8 @@ def run_decode(args):
                    "q_heads": spec.q_heads, "head_dim": d},
         "roofline": {"bound": "hbm", "kernel": "paged_decode", "achieved": best["GBps"],
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(best["GBps"] / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(best["GBps"] / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic_from_profile("paged_decode", "decode_8b_32L_8kv_32q"),
                      "alg_bytes_per_launch": round(b_plain)},
         "cases": res,
     }), flush=True)
@@ -733,7 +737,7 @@ def main():
                          "alg_GBps": round(b / (avg * 1e-3) / 1e9, 1) if b else None}
     dom = max(kernels, key=lambda x: kernels[x]["avg_ms"] * kernels[x]["launches"])
     dom_ach = kernels[dom]["alg_GBps"]
-    traffic = traffic_from_profile(dom, spec)
+    traffic = traffic_from_profile(dom, spec.name)
     roofline = {"bound": "hbm", "kernel": dom, "achieved": dom_ach,
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(dom_ach / HBM_PEAK_GBPS, 4),
