@@ -776,6 +776,8 @@ def main():
         "roofline": roofline,
         "mfma": mfma,
         "kernels": kernels,
+        # inputs come from torch's device Philox generator: record its build
+        "software": {"torch": torch.__version__, "hip": torch.version.hip},
     }
     if not args.no_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
