@@ -39,7 +39,10 @@
 // other's exp/VALU work. Long contexts (token rows that do not fit beside
 // the default ring in LDS) take a 4-slot ring. The column sweep runs
 // backward: it starts on the blocks the first sweep read last and takes the
-// ones still in the ring without reloading them.
+// ones still in the ring without reloading them. In the column sweep the
+// two waves of a SIMD meet the barrier together, so for two unmasked blocks
+// the second block's MFMAs are issued one by one between the first block's
+// exponentials (fenced with sched_barrier) instead of all before them.
 #include <hip/hip_runtime.h>
 
 #include "zp_device.h"
@@ -309,7 +312,10 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(ScoreArgs a) {
   // Slots are walked with counters: up from 0 forward, down from
   // last mod kRing backward.
   auto needs_load = [&](int s) { return s <= last && !(backward && s < kRing); };
-  auto sweep = [&](auto&& mma, auto&& valu, auto&& after) {
+  // pair(slot_a, slot_b, sa, sb) may take over both blocks of an iteration
+  // (returning true), e.g. to interleave one block's MFMAs with the other's
+  // vector work in one straight-line region.
+  auto sweep = [&](auto&& mma, auto&& valu, auto&& after, auto&& pair) {
     static_assert(kRing >= 4, "double steps need four ring slots");
     const int base = backward && last >= 0 ? last % kRing : 0;
     auto adv = [&](int slot) {
@@ -332,19 +338,21 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(ScoreArgs a) {
         slot_w = adv(slot_w);
       }
       const int slot_b = adv(slot_r);
-      Acc acc_a, acc_b;
-      if (sa <= last) {
-        FragT kc;
-        read_frag(kc, slot_r);
-        mma(kc, sa, acc_a);
+      if (!pair(slot_r, slot_b, sa, sb)) {
+        Acc acc_a, acc_b;
+        if (sa <= last) {
+          FragT kc;
+          read_frag(kc, slot_r);
+          mma(kc, sa, acc_a);
+        }
+        if (sb <= last) {
+          FragT kc;
+          read_frag(kc, slot_b);
+          mma(kc, sb, acc_b);
+        }
+        if (sa <= last) valu(acc_a, tile_of(sa), sa);
+        if (sb <= last) valu(acc_b, tile_of(sb), sb);
       }
-      if (sb <= last) {
-        FragT kc;
-        read_frag(kc, slot_b);
-        mma(kc, sb, acc_b);
-      }
-      if (sa <= last) valu(acc_a, tile_of(sa), sa);
-      if (sb <= last) valu(acc_b, tile_of(sb), sb);
       slot_r = adv(slot_b);
     }
     wait_vm_lgkm0(0);
@@ -352,6 +360,7 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(ScoreArgs a) {
     after(niters);
   };
   auto no_after = [](int) {};
+  auto no_pair = [](int, int, int, int) { return false; };
   // logits of this wave's rows against one block (plus, when asked, the
   // block's 16x16 key Gram matrix)
   auto logits = [&](const FragT& kc, Acc& acc, bool gram) {
@@ -427,7 +436,7 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(ScoreArgs a) {
       cs = zpd::pairsum32(cs);
       if (jg == 0 && nl < cnt) s_tok[t] = cnt >= 2 ? cs / (cnt - 1) : 0.f;
     }
-  }, no_after);
+  }, no_after, no_pair);
   // the 16 lanes sharing rows share the reference: their sums just add up
 #pragma unroll
   for (int rt = 0; rt < RTW; ++rt)
@@ -477,7 +486,7 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(ScoreArgs a) {
           m[rt][i] = up ? x : m[rt][i];
         }
       }
-    }, no_after);
+    }, no_after, no_pair);
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
@@ -528,23 +537,17 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(ScoreArgs a) {
     const int t = tile_of(s) * kB + nl;
     if (t < n) a.attn[urow + t] = (cs + xchg[kq][s & 3][nl]) * inv_rows;
   };
-  backward = true;
-  sweep([&](const FragT& kc, int, Acc& acc) { logits(kc, acc, false); },
-        [&](const Acc& acc, int kt, int s) {
-    const int t = kt * kB + nl;
+  // this lane's share of the column sums of an unmasked block
+  auto colsum = [&](const Acc& acc) {
     float cs = 0.f;
-    if (!tile_masked(kt)) {
 #pragma unroll
-      for (int rt = 0; rt < RTW; ++rt)
+    for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) cs += zpd::fast_exp2(fmaf(acc.a[rt][i], sl2, -mp[rt][i]));
-    } else {
-#pragma unroll
-      for (int rt = 0; rt < RTW; ++rt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (entry_ok(rt, i, t)) cs += zpd::fast_exp2(fmaf(acc.a[rt][i], sl2, -mp[rt][i]));
-    }
+      for (int i = 0; i < 4; ++i) cs += zpd::fast_exp2(fmaf(acc.a[rt][i], sl2, -mp[rt][i]));
+    return cs;
+  };
+  // whole-column sum of the wave's rows: to xchg (second half) or kept
+  auto emit = [&](float cs, int s) {
     cs = zpd::pairsum16(cs);
     cs = zpd::pairsum32(cs);
     if (rg == 1) {
@@ -552,12 +555,70 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(ScoreArgs a) {
     } else {
       cs_prev[s & 1] = cs;
     }
+  };
+  backward = true;
+  sweep([&](const FragT& kc, int, Acc& acc) { logits(kc, acc, false); },
+        [&](const Acc& acc, int kt, int s) {
+    const int t = kt * kB + nl;
+    float cs = 0.f;
+    if (!tile_masked(kt)) {
+      cs = colsum(acc);
+    } else {
+#pragma unroll
+      for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (entry_ok(rt, i, t)) cs += zpd::fast_exp2(fmaf(acc.a[rt][i], sl2, -mp[rt][i]));
+    }
+    emit(cs, s);
   }, [&](int i) {  // complete the blocks of iteration i-1
     if (i == 0 || rg != 0 || jg != 0) return;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int s = 2 * (i - 1) + e;
       if (s <= last) finish(s, cs_prev[e]);
+    }
+  }, [&](int slot_a, int slot_b, int sa, int sb) {
+    // two unmasked blocks: block b's MFMAs are interleaved with block a's
+    // exponentials (the two waves of a SIMD reach this point together, so
+    // without it each pays MFMA a, MFMA b, vector a, vector b in series).
+    // bf16 only, up to 8 row tiles (beyond that the registers of both blocks
+    // do not fit beside it).
+    if constexpr (RT > 8 || E::kBytes != 2) {
+      return false;
+    } else {
+      if (sb > last || tile_masked(tile_of(sa)) || tile_masked(tile_of(sb))) return false;
+      FragT ka, kb;
+      read_frag(ka, slot_a);
+      read_frag(kb, slot_b);
+      Acc acc_a, acc_b;
+      logits(ka, acc_a, false);
+      // each of b's MFMAs (k-chunk c of row tile rt, chunk-major so the four
+      // accumulation chains alternate) is followed by an equal share of a's
+      // entries (fma, exp2, add each); the fences keep that order
+      constexpr int kPer = 4 / FragT::kChunks;  // entries of a per MFMA of b
+      float ca = 0.f;
+#pragma unroll
+      for (int rt = 0; rt < RTW; ++rt) acc_b.a[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < FragT::kChunks; ++c)
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt) {
+          if (rt < nrt)
+            acc_b.a[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(zpd::bf16x8_t, q[rt].v[c]),
+                __builtin_bit_cast(zpd::bf16x8_t, kb.v[c]), acc_b.a[rt], 0, 0, 0);
+#pragma unroll
+          for (int x = 0; x < kPer; ++x) {
+            const int e = (c * RTW + rt) * kPer + x;  // entry (e / 4, e % 4) of a
+            ca += zpd::fast_exp2(fmaf(acc_a.a[e / 4][e % 4], sl2, -mp[e / 4][e % 4]));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      const float cb = colsum(acc_b);
+      emit(ca, sa);
+      emit(cb, sb);
+      return true;
     }
   });
   __syncthreads();  // the attention row is complete (same workgroup, via L2)
