@@ -113,6 +113,10 @@ zp_status make_geom(const zp_kv_pool* pool, const zp_params* p,
   if (!p || !b) return fail(ZP_EINVAL, "params/batch is NULL");
   if (b->num_reqs < 0) return fail(ZP_EINVAL, "num_reqs < 0");
   if (p->n_max < 2) return fail(ZP_EINVAL, "n_max must be >= 2");
+  // n_max * b <= n_cap <= 16384 (b = 16): larger caps are not supported, and
+  // bounding n_max here keeps the products below within int range
+  if (p->n_max > 1024)
+    return fail(ZP_EUNSUPPORTED, "n_max %d > 1024 (n_cap is at most 16384)", p->n_max);
   if (p->q_heads <= 0 || p->q_heads % pool->kv_heads)
     return fail(ZP_EINVAL, "q_heads %d is not a positive multiple of kv_heads %d",
                 p->q_heads, pool->kv_heads);

@@ -178,6 +178,8 @@ def _compress(pool=None, batch=None, params=None, ws_bytes=1 << 20,
     (dict(params=_params(q_heads=7)), Z.ZP_EINVAL),
     (dict(params=_params(q_dtype=Z.ZP_F32)), Z.ZP_EUNSUPPORTED),
     (dict(params=_params(n_max=1)), Z.ZP_EINVAL),
+    (dict(params=_params(n_max=1025)), Z.ZP_EUNSUPPORTED),  # n_max * b > 16384
+    (dict(params=_params(n_max=(1 << 31) - 1)), Z.ZP_EUNSUPPORTED),  # no int overflow
     (dict(params=_params(window=0)), Z.ZP_EINVAL),
     (dict(params=_params(flags=1 << 7)), Z.ZP_EINVAL),
     (dict(params=_params(window=49, flags=Z.ZP_PROTECT_WINDOW)), Z.ZP_EINVAL),
