@@ -79,9 +79,10 @@ typedef struct {
 } zp_kv_pool;
 
 /* Parameters of one compression call.
- *   n_max    -- N_max, the per-request block cap; a request compresses when
- *               it holds N_max full blocks and keeps k = (N_max-1)*b tokens
- *               in its first N_max-1 blocks ([zh] §2.1, [de] §2).
+ *   n_max    -- N_max, the per-request block cap, 2..1024 (N_max*b is at
+ *               most 16384); a request compresses when it holds N_max full
+ *               blocks and keeps k = (N_max-1)*b tokens in its first N_max-1
+ *               blocks ([zh] §2.1, [de] §2).
  *   window   -- w, the number of most recent query states used to score
  *               ([zh] §2.1, [de] §2, [es] §2).
  *   q_heads  -- query heads; must be a multiple of kv_heads. Query head
@@ -384,7 +385,8 @@ typedef struct {
   int32_t window;       /* w                                                */
   int32_t query_slots;  /* M                                                */
   int32_t max_running;  /* cap on running requests                          */
-  int32_t max_blocks;   /* table row width; >= ceil((prompt+gen)/b) of all  */
+  int32_t max_blocks;   /* table row width; >= ceil((prompt+gen)/b) of all;
+                           max_blocks * block_size <= 2^30              */
 } zp_sched_config;
 
 typedef struct {

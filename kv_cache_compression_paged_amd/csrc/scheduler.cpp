@@ -123,9 +123,13 @@ int32_t blocks_for(int64_t tokens, int32_t b) {
 extern "C" {
 
 zp_sched* zp_sched_create(const zp_sched_config* cfg) {
+  // token counts are int32: every per-request length is at most
+  // max_blocks * block_size, which must stay well inside that range
   if (!cfg || cfg->num_blocks < 1 || cfg->block_size < 1 || cfg->n_max < 2 ||
+      cfg->max_blocks < cfg->n_max ||
+      static_cast<int64_t>(cfg->max_blocks) * cfg->block_size > (1 << 30) ||
       cfg->window < 1 || cfg->window > cfg->n_max * cfg->block_size ||
-      cfg->query_slots < 1 || cfg->max_running < 1 || cfg->max_blocks < cfg->n_max) {
+      cfg->query_slots < 1 || cfg->max_running < 1) {
     zp::set_error("zp_sched_create: bad configuration");
     return nullptr;
   }

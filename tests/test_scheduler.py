@@ -133,3 +133,5 @@ def test_scheduler_rejects_bad_use():
     s.complete()
     with pytest.raises(Z.ZipageError):
         Z.Scheduler(64, 16, 4, 100, 2, 4, 8)   # window beyond n_max * b
+    with pytest.raises(Z.ZipageError):
+        Z.Scheduler(64, 1 << 16, 4, 8, 2, 4, 1 << 16)   # lengths past int32 range
