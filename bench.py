@@ -139,7 +139,7 @@ def cpu_baseline(spec, wl, seconds: float) -> dict:
     """The oracle, unchanged, on a bounded seeded sample of units."""
     import oracle as O
     import torch
-    from threadpoolctl import threadpool_limits
+    from threadpoolctl import threadpool_info
     from kv_cache_compression_paged_amd import synth
     R, L, H, b = spec.requests, spec.layers, spec.kv_heads, spec.block_size
     n, k = spec.n_tokens, spec.keep
@@ -149,36 +149,41 @@ def cpu_baseline(spec, wl, seconds: float) -> dict:
     p = O.Params(n_max=spec.n_max, block_size=b, window=spec.window)
     tab = torch.from_numpy(wl.tables).to(wl.k_pool.device)
     done, t_cpu = 0, 0.0
-    with threadpool_limits(limits=1):
-        for u in order:
-            if t_cpu >= seconds and done >= 2:
-                break
-            u = int(u)
-            r, l, h = u // (L * H), (u // H) % L, u % H
-            blocks = tab[r].long()
-            kr = synth.raw_numpy(wl.k_pool[l, blocks, h].reshape(n, -1))
-            vr = synth.raw_numpy(wl.v_pool[l, blocks, h].reshape(n, -1))
-            q = synth.raw_numpy(wl.q_window[r, l, :, h * G:(h + 1) * G])
-            g = wl.global_scores[r, l, h].cpu().numpy()
-            pk = kr.reshape(1, spec.n_max, 1, b, -1)
-            pv = vr.reshape(1, spec.n_max, 1, b, -1)
-            t0 = time.perf_counter()
-            res = O.score_unit(O.widen(q, spec.dtype), O.widen(kr, spec.dtype),
-                               g.astype(np.float64), n, 0, p)
-            nk, nv = pk.copy(), pv.copy()
-            table = list(range(spec.n_max))
-            O.compact_unit(pk, nk, table, table, 0, 0, res.keep, b)
-            O.compact_unit(pv, nv, table, table, 0, 0, res.keep, b)
-            O.update_global(g, res.attn, res.keep, k)
-            t_cpu += time.perf_counter() - t0
-            done += 1
+    # the oracle as it stands: numpy's BLAS with its own default thread pool
+    blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+    blas_threads = max([i.get("num_threads", 1) for i in blas] or [1])
+    blas_name = ", ".join(f"{i.get('internal_api')} {i.get('version')}" for i in blas) or "none"
+    for u in order:
+        if t_cpu >= seconds and done >= 2:
+            break
+        u = int(u)
+        r, l, h = u // (L * H), (u // H) % L, u % H
+        blocks = tab[r].long()
+        kr = synth.raw_numpy(wl.k_pool[l, blocks, h].reshape(n, -1))
+        vr = synth.raw_numpy(wl.v_pool[l, blocks, h].reshape(n, -1))
+        q = synth.raw_numpy(wl.q_window[r, l, :, h * G:(h + 1) * G])
+        g = wl.global_scores[r, l, h].cpu().numpy()
+        pk = kr.reshape(1, spec.n_max, 1, b, -1)
+        pv = vr.reshape(1, spec.n_max, 1, b, -1)
+        t0 = time.perf_counter()
+        res = O.score_unit(O.widen(q, spec.dtype), O.widen(kr, spec.dtype),
+                           g.astype(np.float64), n, 0, p)
+        nk, nv = pk.copy(), pv.copy()
+        table = list(range(spec.n_max))
+        O.compact_unit(pk, nk, table, table, 0, 0, res.keep, b)
+        O.compact_unit(pv, nv, table, table, 0, 0, res.keep, b)
+        O.update_global(g, res.attn, res.keep, k)
+        t_cpu += time.perf_counter() - t0
+        done += 1
     tokens_per_s = done * n / (L * H) / t_cpu
-    return {"value": tokens_per_s, "unit": "tokens/s", "cores": 1,
+    return {"value": tokens_per_s, "unit": "tokens/s", "cores": blas_threads,
             "kind": "oracle", "cpu": _cpu_model(), "host_cpus": os.cpu_count(),
+            "blas": blas_name,
             "sample": f"{done} seeded (request, layer, kv_head) units of this "
                       f"workload, full oracle chain (score, select, K/V "
-                      f"compaction, global update), {t_cpu:.1f} s on one "
-                      f"thread; a token covers {L * H} units"}
+                      f"compaction, global update), {t_cpu:.1f} s; numpy's "
+                      f"BLAS on up to {blas_threads} threads, the rest of the "
+                      f"oracle on one; a token covers {L * H} units"}
 
 
 def decode_bytes(spec, lens: np.ndarray) -> float:
