@@ -26,6 +26,11 @@
  *     first_hole[u] = -1 (when that output is requested), and records
  *     ZP_EDEVICE in the workspace. zp_update_global leaves such units alone.
  *   - No C++ exception crosses this interface.
+ *   - The calls that enqueue work (zp_compress, zp_update_global, the decode
+ *     and capture calls, zp_redundancy_full) allocate nothing, synchronise
+ *     nothing and issue no memset, so a caller may record them into a HIP
+ *     graph and replay it (per-launch timing, zp_timing_enable, must be off
+ *     while capturing). zp_workspace_error synchronises and stays outside.
  */
 #ifndef ZIPAGE_H
 #define ZIPAGE_H
