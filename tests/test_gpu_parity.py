@@ -605,3 +605,41 @@ def _random_case(seed):
 def test_random_shapes(seed):
     case = _random_case(seed)
     _check(case, f"random shape {seed}, flags {case.flags}")
+
+
+def _random_prefix_case(seed):
+    """A small random shared-prefix configuration: groups of 2-3 requests
+    share their first S blocks; the block manager plans fresh targets."""
+    rng = np.random.default_rng(10_000 + seed)
+    d = int(rng.choice([64, 128]))
+    hkv = int(rng.integers(1, 4))
+    G = int(rng.choice([1, 2, 4, 6]))
+    n_max = int(rng.integers(4, 14))
+    w = int(rng.integers(1, min(n_max * 16, 192 // G) + 1))
+    groups = int(rng.integers(1, 3))
+    R = groups * int(rng.integers(2, 4))
+    L = int(rng.integers(1, 3))
+    flags = int(rng.choice([0, Z.ZP_NONCAUSAL]))
+    protect = rng.random() < 0.3 and n_max - 1 - (w + 15) // 16 >= 1
+    if protect:
+        flags |= Z.ZP_PROTECT_WINDOW
+    s_max = n_max - 1 - ((w + 15) // 16 if protect else 0)
+    S = int(rng.integers(1, s_max + 1))
+    over = [int(x) for x in rng.integers(0, 40, size=R)] if rng.random() < 0.4 else [0] * R
+    extra = sum((n_max * 16 + e + 15) // 16 - n_max for e in over)
+    pool = groups * S + R * (n_max - S) + extra + R * (n_max - 1 - S) + 4
+    spec = synth.scaled(synth.PREFIX, name=f"random_prefix_{seed}", seed=7000 + seed,
+                        requests=R, layers=L, kv_heads=hkv, q_heads=hkv * G, head_dim=d,
+                        n_max=n_max, window=w, groups=groups, shared_blocks=S,
+                        pool_blocks=pool, permute=True, near_dup=True)
+    n = spec.n_tokens
+    return P.Case(spec, flags=flags, n_tokens=[n + e for e in over],
+                  max_blocks=n_max + 3, use_block_manager=True)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_prefix_shapes(seed):
+    case = _random_prefix_case(seed)
+    s = case.spec
+    _check(case, f"random prefix {seed}: R {s.requests} in {s.groups} groups, "
+                 f"S {s.shared_blocks} of {s.n_max}, w {s.window}, flags {case.flags}")
