@@ -8,7 +8,7 @@ Each step asks the native scheduler (``Scheduler``) for a plan and runs it:
   * slots handed out this step get their query ring and global-score row
     cleared;
   * stream C compresses the plan's compress set (``zp_compress`` reading the
-    query rings, then ``zp_update_global``);
+    query rings, with the global-score update in the same kernel);
   * stream D captures the decode set's new queries into the rings of slot
     holders (``zp_capture_queries``) and decodes one token per request with
     the new K/V row appended (``zp_paged_decode_append``);
@@ -32,9 +32,9 @@ from typing import Dict, List, Optional
 
 import numpy as np
 
-from . import (ZP_BF16, ZP_OK, ZP_WINDOW_RING, DeviceBatch, Scheduler, alloc_outputs,
-               alloc_workspace, make_params, make_pool, zp_capture_queries, zp_compress,
-               zp_paged_decode_append, zp_update_global, zp_workspace_error)
+from . import (ZP_BF16, ZP_OK, ZP_UPDATE_GLOBAL, ZP_WINDOW_RING, DeviceBatch, Scheduler,
+               alloc_outputs, alloc_workspace, make_params, make_pool, zp_capture_queries,
+               zp_compress, zp_paged_decode_append, zp_workspace_error)
 
 
 @dataclass
@@ -85,7 +85,8 @@ class Engine:
                                 dtype=torch.bfloat16, device=device)
         self.glob = torch.zeros((c.query_slots, c.layers, c.kv_heads, self.n_cap),
                                 dtype=torch.float32, device=device)
-        self.params = make_params(c.n_max, c.window, c.q_heads, ZP_BF16, flags=ZP_WINDOW_RING)
+        self.params = make_params(c.n_max, c.window, c.q_heads, ZP_BF16,
+                                  flags=ZP_WINDOW_RING | ZP_UPDATE_GLOBAL)
         self.pool = make_pool(self.k_pool, self.v_pool)
         self.ws = alloc_workspace(self.pool, self.params, 1, device)
         self.gen = torch.Generator(device=device)
@@ -195,7 +196,6 @@ class Engine:
             e[0].record(self.sc)
             zp_compress(self.pool, batch, self.ring, self.glob, self.params, out_c, self.ws,
                         self.sc)
-            zp_update_global(self.glob, self.pool, batch, out_c, self.params, self.sc)
             e[1].record(self.sc)
         if D:
             e[2].record(self.sd)
