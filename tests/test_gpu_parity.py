@@ -643,3 +643,56 @@ def test_random_prefix_shapes(seed):
     s = case.spec
     _check(case, f"random prefix {seed}: R {s.requests} in {s.groups} groups, "
                  f"S {s.shared_blocks} of {s.n_max}, w {s.window}, flags {case.flags}")
+
+
+def _random_wide_case(seed):
+    """Wider random shapes: up to 64 blocks per request (many key tiles per
+    quarter), 12 query heads per KV head, overshoot up to 89 tokens, with or
+    without a shared prefix planned by the block manager."""
+    rng = np.random.default_rng(90_000 + seed)
+    prefix = rng.random() < 0.35
+    dtype = "bf16" if (prefix or rng.random() < 0.8) else "f32"
+    d = int(rng.choice([64, 128]))
+    hkv = int(rng.integers(1, 5))
+    G = int(rng.choice([1, 2, 3, 4, 6, 8, 12]))
+    max_rows = 64 if (dtype == "f32" and d == 128) else 192
+    n_max = int(rng.integers(2, 65))
+    w = int(rng.integers(1, min(n_max * 16, max_rows // G) + 1))
+    L = int(rng.integers(1, 4))
+    flags = int(rng.choice([0, Z.ZP_NONCAUSAL]))
+    protect = rng.random() < 0.3 and w <= (n_max - 1) * 16
+    if prefix:
+        groups = int(rng.integers(1, 3))
+        R = groups * int(rng.integers(2, 4))
+        s_max = n_max - 1 - ((w + 15) // 16 if protect else 0)
+        if s_max < 1:
+            protect = False
+            s_max = n_max - 1
+        S = int(rng.integers(1, s_max + 1)) if n_max >= 2 else 0
+    else:
+        groups, R, S = 1, int(rng.integers(1, 5)), 0
+    if protect:
+        flags |= Z.ZP_PROTECT_WINDOW
+    over = [int(x) for x in rng.integers(0, 90, size=R)] if rng.random() < 0.4 else [0] * R
+    extra = sum((n_max * 16 + e + 15) // 16 - n_max for e in over)
+    if prefix:
+        pool = groups * S + R * (n_max - S) + extra + R * (n_max - 1 - S) + 4
+        base = synth.PREFIX
+    else:
+        pool = R * n_max + extra + 2
+        base = synth.TINY if dtype == "f32" else synth.EIGHT_B
+    spec = synth.scaled(base, name=f"wide_{seed}", seed=9000 + seed, requests=R, layers=L,
+                        kv_heads=hkv, q_heads=hkv * G, head_dim=d, n_max=n_max, window=w,
+                        groups=groups, shared_blocks=S, pool_blocks=pool, permute=True,
+                        near_dup=(dtype == "bf16"))
+    n = spec.n_tokens
+    return P.Case(spec, flags=flags, n_tokens=[n + e for e in over],
+                  max_blocks=n_max + 6, use_block_manager=prefix)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_wide_shapes(seed):
+    case = _random_wide_case(seed)
+    s = case.spec
+    _check(case, f"wide random {seed}: n_max {s.n_max}, w {s.window}, "
+                 f"G {s.q_heads // s.kv_heads}, S {s.shared_blocks}, flags {case.flags}")
