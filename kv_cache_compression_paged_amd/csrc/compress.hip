@@ -593,9 +593,10 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(ScoreArgs a) {
       read_frag(kb, slot_b);
       Acc acc_a, acc_b;
       logits(ka, acc_a, false);
-      // each of b's MFMAs (k-chunk c of row tile rt, chunk-major so the four
-      // accumulation chains alternate) is followed by an equal share of a's
-      // entries (fma, exp2, add each); the fences keep that order
+      // each of b's MFMAs (k-chunk c of row tile rt, chunk-major so that
+      // consecutive MFMAs feed different row tiles' accumulators) is followed
+      // by an equal share of a's entries (fma, exp2, add each), taken in the
+      // order colsum() sums them; the fences keep that order
       constexpr int kPer = 4 / FragT::kChunks;  // entries of a per MFMA of b
       float ca = 0.f;
 #pragma unroll
