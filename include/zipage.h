@@ -51,6 +51,9 @@ typedef int32_t zp_status;
 #define ZP_ENOSPACE     -4  /* free list exhausted (no state was changed)    */
 #define ZP_EHIP         -5  /* the HIP runtime reported an error             */
 #define ZP_EDEVICE      -6  /* a kernel found a bad device table entry       */
+#define ZP_ESYNC        -7  /* workgroups of a split unit stopped waiting on
+                               each other (bounded wait passed); the call's
+                               outputs are incomplete                        */
 
 /* element types */
 #define ZP_F32  0
@@ -66,6 +69,10 @@ typedef int32_t zp_status;
                                        score update of zp_update_global in
                                        the same kernel (then that call must
                                        not follow for this batch)            */
+#define ZP_SPLIT_UNITS    (1u << 4) /* zp_compress spreads every unit over up
+                                       to 8 workgroups where that schedule
+                                       applies (same results, up to the
+                                       rounding of the attention sums)       */
 
 /* A paged KV pool: k and v are device arrays laid out
  * [layers][num_blocks][kv_heads][block_size][head_dim] of `dtype`, 16-byte
@@ -164,8 +171,13 @@ typedef struct {
   int32_t* first_hole;
 } zp_compress_out;
 
-/* Bytes of device workspace zp_compress needs for num_reqs requests (256:
- * the device error word and padding, whatever the batch).
+/* Bytes of device workspace zp_compress needs for num_reqs requests with
+ * these params: 256 (the error word and padding), or, with ZP_SPLIT_UNITS on
+ * a bf16 pool, the split-unit schedule's size (about 11.5 MB, whatever the
+ * batch: the error word, a group ticket and 256 group exchange slots).
+ * zp_compress also accepts a 256-byte workspace with ZP_SPLIT_UNITS; it then
+ * runs the one-workgroup schedule. A workspace serves one call at a time:
+ * calls that may overlap (on different streams) need their own.
  * Errors: ZP_EINVAL for a NULL argument or non-positive sizes. */
 zp_status zp_compress_workspace_bytes(const zp_kv_pool* pool,
                                       const zp_params* params,
@@ -189,6 +201,16 @@ zp_status zp_compress_workspace_bytes(const zp_kv_pool* pool,
  * here unless ZP_UPDATE_GLOBAL is set, then updated in place as by
  * zp_update_global). workspace: device, 256-byte aligned, at least
  * zp_compress_workspace_bytes; it also receives the device error word.
+ * Schedules. By default one workgroup scores, selects and compacts a whole
+ * unit. With ZP_SPLIT_UNITS, a bf16 call with n_cap <= 4096 (w*G <= 128) or
+ * n_cap <= 2048 (w*G <= 192) and a workspace of zp_compress_workspace_bytes
+ * splits every unit over up to 8 workgroups, one per slice of 512 (256)
+ * tokens: each keeps its slice's keys on chip, the workgroups exchange their
+ * per-row softmax normalisers and their eviction candidates through the
+ * workspace, and every K/V row is read once. Both give the same keep sets and bytes; attention values may differ
+ * in the last bits (summation order). The split schedule's waits on other
+ * workgroups are bounded: if one ever passes its limit (a few seconds), the
+ * kernel stops and the workspace error word becomes ZP_ESYNC.
  * Errors: ZP_EINVAL, ZP_EUNSUPPORTED (head_dim not 64/128, block_size not 16,
  * w*G > 192 -- 64 for fp32 with head_dim 128 --, n_cap > 16384, or, for fp32
  * with head_dim 128 only, n_cap above about 6100: the per-token scores of a
@@ -209,8 +231,8 @@ zp_status zp_update_global(float* global_scores, const zp_kv_pool* pool,
                            const zp_params* params, void* stream);
 
 /* Reads the device error word of a workspace after the caller's stream work
- * has finished: synchronises `stream`, stores ZP_OK or ZP_EDEVICE in *code
- * and clears the word. Errors: ZP_EINVAL, ZP_EHIP. */
+ * has finished: synchronises `stream`, stores ZP_OK, ZP_EDEVICE or ZP_ESYNC
+ * in *code and clears the word. Errors: ZP_EINVAL, ZP_EHIP. */
 zp_status zp_workspace_error(void* workspace, void* stream, int32_t* code);
 
 /* Decode attention over a paged cache, the consumer of the compressed blocks

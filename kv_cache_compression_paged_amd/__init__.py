@@ -29,6 +29,7 @@ ZP_EWORKSPACE = -3
 ZP_ENOSPACE = -4
 ZP_EHIP = -5
 ZP_EDEVICE = -6
+ZP_ESYNC = -7
 
 ZP_F32 = 0
 ZP_BF16 = 1
@@ -37,6 +38,7 @@ ZP_NONCAUSAL = 1 << 0
 ZP_PROTECT_WINDOW = 1 << 1
 ZP_WINDOW_RING = 1 << 2
 ZP_UPDATE_GLOBAL = 1 << 3
+ZP_SPLIT_UNITS = 1 << 4
 
 ZP_KERNEL_COMPRESS = 0
 ZP_KERNEL_GLOBAL = 1
@@ -105,7 +107,7 @@ _lib = None
 def _status_name(status: int) -> str:
     names = {0: "ZP_OK", -1: "ZP_EINVAL", -2: "ZP_EUNSUPPORTED",
              -3: "ZP_EWORKSPACE", -4: "ZP_ENOSPACE", -5: "ZP_EHIP",
-             -6: "ZP_EDEVICE"}
+             -6: "ZP_EDEVICE", -7: "ZP_ESYNC"}
     return names.get(status, f"status {status}")
 
 

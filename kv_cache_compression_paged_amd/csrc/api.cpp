@@ -127,7 +127,8 @@ zp_status make_geom(const zp_kv_pool* pool, const zp_params* p,
   if (!std::isfinite(p->w_attn) || !std::isfinite(p->w_global) ||
       !std::isfinite(p->w_red) || !std::isfinite(p->sm_scale))
     return fail(ZP_EINVAL, "score weights and scale must be finite");
-  if (p->flags & ~(ZP_NONCAUSAL | ZP_PROTECT_WINDOW | ZP_WINDOW_RING | ZP_UPDATE_GLOBAL))
+  if (p->flags & ~(ZP_NONCAUSAL | ZP_PROTECT_WINDOW | ZP_WINDOW_RING | ZP_UPDATE_GLOBAL |
+                   ZP_SPLIT_UNITS))
     return fail(ZP_EINVAL, "unknown flags 0x%x", p->flags);
   const int k = (p->n_max - 1) * pool->block_size;
   if ((p->flags & ZP_PROTECT_WINDOW) && p->window > k)
@@ -170,12 +171,13 @@ zp_status make_geom(const zp_kv_pool* pool, const zp_params* p,
   return ZP_OK;
 }
 
-// workspace: [0,256) error word; then hole[U] int32
+// workspace: [0,256) error word; with ZP_SPLIT_UNITS on a bf16 pool, then
+// the split-unit schedule's ticket, abort flag and group exchange slots
 constexpr size_t kWsHeader = 256;
 
-size_t workspace_for(int64_t units) {
-  (void)units;
-  return kWsHeader;
+size_t workspace_for(const zp_kv_pool* pool, const zp_params* params) {
+  return (pool->dtype == ZP_BF16 && (params->flags & ZP_SPLIT_UNITS)) ? split_workspace_bytes()
+                                                                      : kWsHeader;
 }
 
 }  // namespace
@@ -192,7 +194,7 @@ zp_status zp_compress_workspace_bytes(const zp_kv_pool* pool,
     return fail(ZP_EINVAL, "zp_compress_workspace_bytes: bad arguments");
   if (pool->layers <= 0 || pool->kv_heads <= 0)
     return fail(ZP_EINVAL, "zp_compress_workspace_bytes: bad pool sizes");
-  *bytes = workspace_for(static_cast<int64_t>(num_reqs) * pool->layers * pool->kv_heads);
+  *bytes = workspace_for(pool, params);
   return ZP_OK;
 }
 
@@ -208,16 +210,19 @@ zp_status zp_compress(const zp_kv_pool* pool, const zp_batch* batch,
                 "attn are required");
   if (!aligned16(q_window))
     return fail(ZP_EINVAL, "zp_compress: q_window must be 16-byte aligned");
-  const int64_t units = static_cast<int64_t>(g.R) * g.L * g.Hkv;
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u))
     return fail(ZP_EWORKSPACE, "zp_compress: workspace NULL or not 256-byte aligned");
-  if (workspace_bytes < workspace_for(units))
+  if (workspace_bytes < kWsHeader)
     return fail(ZP_EWORKSPACE, "zp_compress: workspace %zu < %zu bytes",
-                workspace_bytes, workspace_for(units));
+                workspace_bytes, kWsHeader);
   if (g.R == 0) return ZP_OK;
   int32_t* err = static_cast<int32_t*>(workspace);
   timing_before(ZP_KERNEL_COMPRESS, stream);
-  st = launch_compress(g, *pool, *batch, q_window, global_scores, *out, err, stream);
+  if (split_eligible(g, workspace_bytes))
+    st = launch_compress_split(g, *pool, *batch, q_window, global_scores, *out, workspace,
+                               stream);
+  else
+    st = launch_compress(g, *pool, *batch, q_window, global_scores, *out, err, stream);
   timing_after(ZP_KERNEL_COMPRESS, stream);
   return st;
 }

@@ -30,6 +30,14 @@ zp_status launch_compress(const CompressGeom& g, const zp_kv_pool& pool,
                           const zp_batch& batch, const void* q_window,
                           float* global_scores,
                           const zp_compress_out& out, int32_t* err, void* stream);
+// Split-unit schedule (compress_split.hip): workspace size, whether a call
+// can use it, and its launcher (the workspace holds the error word first).
+size_t split_workspace_bytes();
+bool split_eligible(const CompressGeom& g, size_t workspace_bytes);
+zp_status launch_compress_split(const CompressGeom& g, const zp_kv_pool& pool,
+                                const zp_batch& batch, const void* q_window,
+                                float* global_scores, const zp_compress_out& out,
+                                void* workspace, void* stream);
 zp_status launch_global(const CompressGeom& g, float* global_scores,
                         const zp_batch& batch, const int32_t* keep,
                         const float* attn, void* stream);

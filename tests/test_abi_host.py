@@ -204,10 +204,26 @@ def test_compress_empty_batch_is_a_no_op():
 
 
 def test_workspace_size_formula():
-    # the error word only: compaction runs inside the scoring kernel, so no
-    # per-unit hand-over array is needed
+    # the error word only (compaction runs inside the scoring kernel, so no
+    # per-unit hand-over array is needed); with ZP_SPLIT_UNITS on bf16, the
+    # split-unit schedule's error word, ticket and abort flag, and 256 group
+    # exchange slots of 8 parts x (192 rows + 512 candidates) 64-bit words,
+    # whatever the batch
     assert Z.zp_compress_workspace_bytes(_pool(), _params(), 2) == 256
     assert Z.zp_compress_workspace_bytes(_pool(), _params(), 100) == 256
+    split = 512 + 256 * (8 * 192 * 8 + 8 * 512 * 8)
+    sp = _params(flags=Z.ZP_SPLIT_UNITS)
+    assert Z.zp_compress_workspace_bytes(_pool(), sp, 2) == split
+    assert Z.zp_compress_workspace_bytes(_pool(), sp, 100) == split
+    f32 = _pool(dtype=Z.ZP_F32)
+    assert Z.zp_compress_workspace_bytes(
+        f32, _params(q_dtype=Z.ZP_F32, flags=Z.ZP_SPLIT_UNITS), 2) == 256
+
+
+def test_split_flag_is_accepted_and_other_bits_are_not():
+    assert _compress(params=_params(flags=Z.ZP_SPLIT_UNITS),
+                     batch=_batch(num_reqs=0)) == Z.ZP_OK
+    assert _compress(params=_params(flags=1 << 5), batch=_batch(num_reqs=0)) == Z.ZP_EINVAL
 
 
 def test_decode_rejects_bad_arguments():

@@ -1,0 +1,175 @@
+"""GPU parity of the split-unit schedule (ZP_SPLIT_UNITS), where one unit's
+key slices are scored by up to 8 workgroups that exchange row normalisers and
+eviction candidates, against the CPU oracle.
+
+The cases are sized so that units really span several slices (512 tokens,
+256 with 192 window rows): 8 parts, a ragged last part, E larger than a slice,
+slices wholly pinned by a shared prefix, all tokens tied, evictions on slice
+boundaries, and enough units that every group exchange slot is reused. Each
+goes through tests/parity.py (every unit element by element, pools byte for
+byte); a few run again without the flag, on the one-workgroup schedule.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_compression_paged_amd as Z
+from kv_cache_compression_paged_amd import synth
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+SPLIT = Z.ZP_SPLIT_UNITS
+
+
+def _check(case, label):
+    _say(f"[split] {label}: {case.spec} flags={case.flags}")
+    res = P.run_case(case)
+    _say(f"[split] {label}: ok={res.ok} stats={res.stats}")
+    assert res.ok, "\n".join(res.failures)
+
+
+# 8 parts of 512 tokens (w*G = 128)
+FULL = synth.scaled(synth.EIGHT_B, requests=2, layers=1, kv_heads=2, q_heads=8,
+                    n_max=256, pool_blocks=2 * 256 + 8)
+# 192 window rows: 8 parts of 256 tokens
+ROWS192 = synth.scaled(synth.SMALL, requests=1, layers=1, n_max=128,
+                       pool_blocks=128 + 8)
+D64 = synth.scaled(FULL, head_dim=64, near_dup=False)
+PREFIX = synth.scaled(synth.PREFIX, requests=2, layers=1, kv_heads=2, q_heads=8,
+                      n_max=256, groups=1, shared_blocks=40,
+                      pool_blocks=40 + 2 * 216 + 2 * 215 + 5)
+OVER = synth.scaled(FULL, n_max=200, pool_blocks=2 * 200 + 8 + 48)
+
+
+def _forced_global(spec, positions):
+    g = np.zeros((spec.requests, spec.layers, spec.kv_heads, spec.n_tokens))
+    g[..., list(positions)] = -100.0
+    return g
+
+
+CASES = [
+    ("8 parts", P.Case(FULL, flags=SPLIT)),
+    ("4 parts, ragged last slice", P.Case(synth.scaled(FULL, n_max=100, pool_blocks=208),
+                                          flags=SPLIT)),
+    ("overshoot, E = 616 > slice", P.Case(OVER, flags=SPLIT,
+                                          n_tokens=[OVER.n_tokens + 600, OVER.n_tokens + 37],
+                                          max_blocks=OVER.n_max + 38)),
+    ("overshoot, tail slice inside the causal window", P.Case(
+        synth.scaled(synth.EIGHT_B, requests=3, layers=2, kv_heads=2, q_heads=8, n_max=32,
+                     pool_blocks=112 + 12),
+        flags=SPLIT, n_tokens=[512 + 5, 512 + 16, 512 + 37], max_blocks=35)),
+    ("192 rows, 8 parts of 256", P.Case(ROWS192, flags=SPLIT)),
+    ("head_dim 64, 8 parts", P.Case(D64, flags=SPLIT)),
+    ("shared prefix over 1.25 slices", P.Case(PREFIX, flags=SPLIT, use_block_manager=True)),
+    ("non-causal, protected window", P.Case(
+        FULL, flags=SPLIT | Z.ZP_NONCAUSAL | Z.ZP_PROTECT_WINDOW)),
+    ("evict block 0: every later row shifts",
+     P.Case(FULL, flags=SPLIT, global_override=_forced_global(FULL, range(16)))),
+    ("evictions on slice boundaries",
+     P.Case(FULL, flags=SPLIT, global_override=_forced_global(
+         FULL, [511, 512, 1023, 1024, 1535, 2047, 2048, 2559, 3071, 3072, 3583, 3584,
+                4079, 4080, 4094, 4095]))),
+    ("outlier key x100", P.Case(synth.scaled(FULL, requests=1), flags=SPLIT,
+                                outlier=(700, 100.0))),
+]
+
+
+@pytest.mark.parametrize("label,case", CASES, ids=[c[0] for c in CASES])
+def test_split_schedule(label, case):
+    _check(case, label)
+
+
+@pytest.mark.parametrize("label,case", [CASES[0], CASES[2], CASES[5]],
+                         ids=[CASES[i][0] for i in (0, 2, 5)])
+def test_single_workgroup_schedule(label, case):
+    c = P.Case(**{**case.__dict__, "flags": case.flags & ~SPLIT})
+    _check(c, label + " (one workgroup per unit)")
+
+
+def test_all_tokens_tied():
+    # identical keys, constant global scores, no mask: every score is equal,
+    # every token of every slice is a candidate (the union holds all 4096),
+    # and the first k positions are kept
+    spec = synth.scaled(FULL, requests=1)
+    g = np.full((1, 1, spec.kv_heads, spec.n_tokens), 0.25)
+    case = P.Case(spec, flags=SPLIT | Z.ZP_NONCAUSAL, identical_keys=True, global_override=g)
+    _check(case, "all tokens tied")
+
+
+def test_exchange_slots_reused():
+    # 320 units of 2 parts over at most 128 groups: every group's exchange
+    # slot serves several units in a row
+    spec = synth.scaled(synth.EIGHT_B, requests=10, layers=4, n_max=64,
+                        pool_blocks=10 * 64 + 8)
+    _check(P.Case(spec, flags=SPLIT), "320 units, exchange slots reused")
+
+
+def test_fused_global_update_is_bit_identical_split():
+    """ZP_UPDATE_GLOBAL in the split schedule: each part updates the global
+    scores of its own kept tokens; the result equals zp_compress followed by
+    zp_update_global bit for bit, and so do pools, keep sets and attention."""
+    case = P.Case(OVER, flags=SPLIT, n_tokens=[OVER.n_tokens + 600, OVER.n_tokens + 37],
+                  max_blocks=OVER.n_max + 38)
+    spec = case.spec
+    wl, glob, host, dev, tables, dst, pinned, n_tok, _ = P.build_inputs(case)
+    R, L, H = spec.requests, spec.layers, spec.kv_heads
+    U, k = R * L * H, spec.keep
+    zparams, _ = P._params_for(spec, SPLIT)
+    fparams, _ = P._params_for(spec, SPLIT | Z.ZP_UPDATE_GLOBAL)
+    res = []
+    for fused in (False, True):
+        kp, vp, g = wl.k_pool.clone(), wl.v_pool.clone(), glob.clone()
+        pool = Z.make_pool(kp, vp)
+        out = Z.alloc_outputs(U, k, dev.n_cap, "cuda")
+        ws = Z.alloc_workspace(pool, zparams, R, "cuda")
+        if fused:
+            Z.zp_compress(pool, dev, wl.q_window, g, fparams, out, ws)
+        else:
+            Z.zp_compress(pool, dev, wl.q_window, g, zparams, out, ws)
+            Z.zp_update_global(g, pool, dev, out, zparams)
+        torch.cuda.synchronize()
+        assert Z.zp_workspace_error(ws) == Z.ZP_OK
+        res.append((kp, vp, g, out))
+    (k1, v1, g1, o1), (k2, v2, g2, o2) = res
+    assert torch.equal(k1, k2) and torch.equal(v1, v2)
+    assert torch.equal(g1.view(torch.int32), g2.view(torch.int32))
+    assert torch.equal(o1.keep_idx, o2.keep_idx)
+    for u in range(U):
+        nu = int(n_tok[u // (L * H)])
+        assert torch.equal(o1.attn[u, :nu].view(torch.int32), o2.attn[u, :nu].view(torch.int32))
+    _say("[split] fused global update: bit-identical")
+
+
+def test_small_workspace_takes_the_one_workgroup_schedule():
+    """With ZP_SPLIT_UNITS a 256-byte workspace is still accepted: the call
+    runs the one-workgroup schedule, with the same results."""
+    case = P.Case(synth.scaled(FULL, requests=1))
+    spec = case.spec
+    wl, glob, host, dev, tables, dst, pinned, n_tok, _ = P.build_inputs(case)
+    U, k = spec.layers * spec.kv_heads, spec.keep
+    zparams, _ = P._params_for(spec, SPLIT)
+    keeps = []
+    for ws_bytes in (256, None):
+        kp, vp, g = wl.k_pool.clone(), wl.v_pool.clone(), glob.clone()
+        pool = Z.make_pool(kp, vp)
+        out = Z.alloc_outputs(U, k, dev.n_cap, "cuda")
+        ws = (torch.zeros(64, dtype=torch.int32, device="cuda") if ws_bytes
+              else Z.alloc_workspace(pool, zparams, 1, "cuda"))
+        Z.zp_compress(pool, dev, wl.q_window, g, zparams, out, ws)
+        torch.cuda.synchronize()
+        assert Z.zp_workspace_error(ws) == Z.ZP_OK
+        keeps.append((out.keep_idx.clone(), kp, vp))
+    # the two schedules sum attention in different orders; on this seeded
+    # input no score lies near the threshold, so keep sets and bytes agree
+    assert torch.equal(keeps[0][0], keeps[1][0])
+    assert torch.equal(keeps[0][1], keeps[1][1]) and torch.equal(keeps[0][2], keeps[1][2])
