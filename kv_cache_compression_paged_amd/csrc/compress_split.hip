@@ -436,22 +436,24 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
     // ---- masked logits; per-row slice maximum and exp2 sums. Masked entries
     // (past n, or after a row's position) become -inf by a select (a
     // divergent conditional store into the accumulator was observed to leave
-    // some of them in place); the scale goes into the exponent's fma
+    // some of them in place), in the blocks that hold any; the scale goes
+    // into the exponent's fma
     const float sl2 = a.sl2;  // > 0
 #pragma unroll
     for (int b = 0; b < SB; ++b) {
       const int kb_g = p * SB + b;
       const bool full = b < nb_here && (kb_g + 1) * kB <= n &&
                         (!causal || kb_g * kB + kB - 1 <= n - a.w);
-      const int tt = kb_g * kB + nl;
+      if (!full) {  // uniform: only blocks that hold masked entries
+        const int tt = kb_g * kB + nl;
 #pragma unroll
-      for (int i = 0; i < RTW; ++i)
+        for (int i = 0; i < RTW; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          bool ok = full;
-          if (!full) ok = b < nb_here && tt < n && (causal ? tt <= rp[i][j] : rp[i][j] >= 0);
-          acc[i][b][j] = ok ? acc[i][b][j] : -INFINITY;
-        }
+          for (int j = 0; j < 4; ++j) {
+            const bool ok = b < nb_here && tt < n && (causal ? tt <= rp[i][j] : rp[i][j] >= 0);
+            acc[i][b][j] = ok ? acc[i][b][j] : -INFINITY;
+          }
+      }
     }
     float mloc[RTW][4];
     float lsum[RTW][4];
