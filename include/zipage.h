@@ -207,7 +207,10 @@ zp_status zp_compress_workspace_bytes(const zp_kv_pool* pool,
  * splits every unit over up to 8 workgroups, one per slice of 512 (256)
  * tokens: each keeps its slice's keys on chip, the workgroups exchange their
  * per-row softmax normalisers and their eviction candidates through the
- * workspace, and every K/V row is read once. Both give the same keep sets and bytes; attention values may differ
+ * workspace, and every K/V row is read once. Its grid holds one workgroup
+ * per CU and the workgroups of a unit wait on each other, so two such calls
+ * must not run concurrently on one device (they could hold every CU between
+ * them and wait until the bounded wait ends with ZP_ESYNC). Both give the same keep sets and bytes; attention values may differ
  * in the last bits (summation order). The split schedule's waits on other
  * workgroups are bounded: if one ever passes its limit (a few seconds), the
  * kernel stops and the workspace error word becomes ZP_ESYNC.

@@ -27,7 +27,7 @@
 //      part selects the unit's exact eviction set from the candidates alone,
 //      and every part knows how many candidates each slice posts.
 // Every exchanged word is a 64-bit relaxed device-scope atomic that carries
-// a tag (the exchange slot's generation), so a reader polls each word until
+// a tag (the group's unit iteration + 1), so a reader polls each word until
 // its tag matches and no release/acquire fence (an L2 write-back) is needed.
 //
 // Ordering hazards of the in-place compaction, and why they cannot occur:
@@ -40,9 +40,13 @@
 // Scheduling: a persistent grid of one workgroup per CU forms groups of P as
 // the workgroups start: each takes an atomic ticket t and becomes part
 // t mod P of group t / P. Group g runs units g, g + NG, g + 2 NG, ... (NG
-// groups), its parts in step with each other. A part only waits on parts
-// that hold tickets, i.e. are resident, so the schedule needs no
-// co-residency guarantee. Each group has its own exchange slot; a word's tag
+// groups), its parts in step with each other. Groups form in the order the
+// workgroups start, so at most one group is incomplete at a time and its
+// parts wait only for the next workgroups of this grid to start, which the
+// hardware does as other work on the device drains. (Two such launches that
+// share the device can hold every CU between them with one incomplete group
+// each; then both wait until the bounded wait below ends.) Each group has
+// its own exchange slot; a word's tag
 // is the group's unit iteration + 1, and since both exchanges of a unit are
 // full barriers of the group, a slot is never rewritten while a part of the
 // group may still read its previous contents. Every wait is bounded: past
