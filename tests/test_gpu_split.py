@@ -173,3 +173,60 @@ def test_small_workspace_takes_the_one_workgroup_schedule():
     # input no score lies near the threshold, so keep sets and bytes agree
     assert torch.equal(keeps[0][0], keeps[1][0])
     assert torch.equal(keeps[0][1], keeps[1][1]) and torch.equal(keeps[0][2], keeps[1][2])
+
+
+def _random_split_case(seed):
+    """Seeded random shapes for the split schedule: up to 8 slices per unit
+    (n_max up to 256), 1 to 12 query heads per KV head, windows up to the
+    192-row limit, head_dim 64 or 128, overshoot up to 90 tokens, either
+    mask, the protected window and shared prefixes, all inside the split
+    schedule's limits (n_cap <= 4096 for up to 128 window rows, else 2048)."""
+    rng = np.random.default_rng(77_000 + seed)
+    prefix = rng.random() < 0.3
+    d = int(rng.choice([64, 128]))
+    hkv = int(rng.integers(1, 3))
+    G = int(rng.choice([1, 2, 4, 6, 8, 12]))
+    w_cap = 192 // G
+    w = int(rng.integers(1, min(64, w_cap) + 1))
+    cap = 4096 if w * G <= 128 else 2048
+    over_max = 90
+    n_max = int(rng.integers(2, (cap - over_max) // 16 + 1))
+    w = min(w, n_max * 16)
+    flags = SPLIT | int(rng.choice([0, Z.ZP_NONCAUSAL]))
+    protect = rng.random() < 0.3 and w <= (n_max - 1) * 16
+    if prefix:
+        groups = 1
+        R = 2
+        s_max = n_max - 1 - ((w + 15) // 16 if protect else 0)
+        if s_max < 1:
+            protect = False
+            s_max = n_max - 1
+        S = int(rng.integers(1, s_max + 1))
+    else:
+        groups, R, S = 1, int(rng.integers(1, 3)), 0
+    if protect:
+        flags |= Z.ZP_PROTECT_WINDOW
+    over = [int(x) for x in rng.integers(0, over_max + 1, size=R)] if rng.random() < 0.4 else [0] * R
+    extra = sum((n_max * 16 + e + 15) // 16 - n_max for e in over)
+    if prefix:
+        pool = groups * S + R * (n_max - S) + extra + R * (n_max - 1 - S) + 4
+        base = synth.PREFIX
+    else:
+        pool = R * n_max + extra + 2
+        base = synth.EIGHT_B
+    spec = synth.scaled(base, name=f"split_{seed}", seed=7000 + seed, requests=R, layers=1,
+                        kv_heads=hkv, q_heads=hkv * G, head_dim=d, n_max=n_max, window=w,
+                        groups=groups, shared_blocks=S, pool_blocks=pool, permute=True,
+                        near_dup=True)
+    n = spec.n_tokens
+    return P.Case(spec, flags=flags, n_tokens=[n + e for e in over],
+                  max_blocks=n_max + 6, use_block_manager=prefix)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_split_shapes(seed):
+    case = _random_split_case(seed)
+    s = case.spec
+    _check(case, f"random split shape {seed}: n_max {s.n_max}, d {s.head_dim}, "
+                 f"G {s.q_heads // s.kv_heads}, w {s.window}, S {s.shared_blocks}, "
+                 f"n {case.n_tokens}")
