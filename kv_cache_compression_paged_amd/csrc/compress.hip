@@ -93,7 +93,7 @@ constexpr int default_slots() {
 }
 constexpr int kLongSlots = 4;
 
-// s_waitcnt with vmcnt = n (0..28), expcnt untouched, lgkmcnt = 0.
+// s_waitcnt with vmcnt = n (0..28 or 32), expcnt untouched, lgkmcnt = 0.
 __device__ __forceinline__ void wait_vm_lgkm0(int n) {
 #define ZP_W(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (((N) >> 4) << 14) | (7 << 4))
   switch (n) {
@@ -106,7 +106,7 @@ __device__ __forceinline__ void wait_vm_lgkm0(int n) {
     case 18: ZP_W(18); break;  case 19: ZP_W(19); break;  case 20: ZP_W(20); break;
     case 21: ZP_W(21); break;  case 22: ZP_W(22); break;  case 23: ZP_W(23); break;
     case 24: ZP_W(24); break;  case 25: ZP_W(25); break;  case 26: ZP_W(26); break;
-    case 27: ZP_W(27); break;  case 28: ZP_W(28); break;
+    case 27: ZP_W(27); break;  case 28: ZP_W(28); break;  case 32: ZP_W(32); break;
     default: ZP_W(0); break;
   }
 #undef ZP_W
@@ -795,7 +795,6 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(ScoreArgs a) {
   const int k = a.k;
   struct Buf {
     zpd::u32x4_t vk[kPasses], vv[kPasses];
-    int64_t doff[kPasses];
   };
   // rows past k are clamped to row k-1 (always valid) and not stored
   auto load_chunk = [&](int c0, Buf& bf) {
@@ -806,40 +805,49 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(ScoreArgs a) {
       const int64_t soff = tab[sp / kB] * block_stride + (sp % kB) * TG::kRowBytes + piece16;
       bf.vk[e] = __builtin_nontemporal_load(reinterpret_cast<const zpd::u32x4_t*>(kmut + soff));
       bf.vv[e] = __builtin_nontemporal_load(reinterpret_cast<const zpd::u32x4_t*>(vmut + soff));
-      bf.doff[e] = dtab[t / kB] * block_stride + (t % kB) * TG::kRowBytes + piece16;
     }
   };
   auto store_chunk = [&](int c0, const Buf& bf) {
 #pragma unroll
-    for (int e = 0; e < kPasses; ++e)
-      if (c0 + e * kRowsPerPass + prow < k) {
-        __builtin_nontemporal_store(bf.vk[e], reinterpret_cast<zpd::u32x4_t*>(kmut + bf.doff[e]));
-        __builtin_nontemporal_store(bf.vv[e], reinterpret_cast<zpd::u32x4_t*>(vmut + bf.doff[e]));
+    for (int e = 0; e < kPasses; ++e) {
+      const int t = c0 + e * kRowsPerPass + prow;
+      if (t < k) {
+        const int64_t doff = dtab[t / kB] * block_stride + (t % kB) * TG::kRowBytes + piece16;
+        __builtin_nontemporal_store(bf.vk[e], reinterpret_cast<zpd::u32x4_t*>(kmut + doff));
+        __builtin_nontemporal_store(bf.vv[e], reinterpret_cast<zpd::u32x4_t*>(vmut + doff));
       }
+    }
   };
-  // Double buffered: the next chunk's loads go out before this chunk's are
-  // awaited (they read rows at or above the next chunk's start, which no
-  // store of this chunk touches). Loads return in order, so at most 2*kPasses
-  // outstanding memory operations means this chunk's loads have landed,
-  // whatever the order in which earlier stores complete; the raw barrier
-  // then holds every lane until all of the chunk is read.
-  auto step = [&](int c0, Buf& cur, Buf& nxt) {
-    const bool more = c0 + kRowsPerChunk < k;
-    if (more) {
-      load_chunk(c0 + kRowsPerChunk, nxt);
+  // Triple buffered: the loads of the two chunks after this one are in
+  // flight while this chunk's are awaited (they read rows at or above their
+  // own chunks' starts, which no store of this chunk touches). Loads return
+  // in order, so at most 2*kPasses outstanding memory operations per later
+  // chunk in flight means this chunk's loads have landed, whatever the order
+  // in which earlier stores complete; the raw barrier then holds every lane
+  // until all of the chunk is read.
+  auto step = [&](int c0, Buf& cur, Buf& nxt2) {
+    const bool more1 = c0 + kRowsPerChunk < k;
+    const bool more2 = c0 + 2 * kRowsPerChunk < k;
+    if (more2) {
+      load_chunk(c0 + 2 * kRowsPerChunk, nxt2);
+      wait_vm_lgkm0(4 * kPasses);
+    } else if (more1) {
       wait_vm_lgkm0(2 * kPasses);
     } else {
       wait_vm_lgkm0(0);
     }
     step_barrier();
     store_chunk(c0, cur);
-    return more;
+    return more1;
   };
-  Buf b0, b1;
+  static_assert(4 * kPasses == 32, "wait count");
+  Buf b0, b1, b2;
   load_chunk(start, b0);
-  for (int c0 = start; c0 < k; c0 += 2 * kRowsPerChunk) {
-    if (!step(c0, b0, b1)) break;
+  if (start + kRowsPerChunk < k) load_chunk(start + kRowsPerChunk, b1);
+  for (int c0 = start; c0 < k; c0 += 3 * kRowsPerChunk) {
+    if (!step(c0, b0, b2)) break;
     if (!step(c0 + kRowsPerChunk, b1, b0)) break;
+    if (!step(c0 + 2 * kRowsPerChunk, b2, b1)) break;
   }
 }
 
