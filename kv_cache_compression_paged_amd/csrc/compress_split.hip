@@ -228,7 +228,6 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int jg = lane >> 4, nl = lane & 15;
   uint32_t* ticket = reinterpret_cast<uint32_t*>(a.ws + kCtlOff);
   uint32_t* abort_flag = ticket + 1;
   const bool causal = (a.flags & ZP_NONCAUSAL) == 0;

@@ -306,10 +306,11 @@ def _sample_units(U, n_samples, seed):
     return sorted(units | {0, U - 1})
 
 
-def _full_size_sampled(spec, n_samples, seed, fused=False):
+def _full_size_sampled(spec, n_samples, seed, fused=False, flags=0):
     """Run the full call and check sampled units against the oracle. With
     fused=True the global update runs inside the compression kernel
-    (ZP_UPDATE_GLOBAL), the launch configuration bench.py times."""
+    (ZP_UPDATE_GLOBAL), the launch configuration bench.py times; `flags` adds
+    schedule bits (ZP_SPLIT_UNITS)."""
     dev = "cuda"
     _say(f"[full] generating {spec.name}")
     wl = synth.make(spec, device=dev)
@@ -333,7 +334,7 @@ def _full_size_sampled(spec, n_samples, seed, fused=False):
         dst, pinned = tables.copy(), np.zeros(R, dtype=np.int32)
     tab_dev = torch.from_numpy(tables).to(dev)
     saved = _save_units(spec, wl, tab_dev, units)
-    zparams, _ = P._params_for(spec, Z.ZP_UPDATE_GLOBAL if fused else 0)
+    zparams, _ = P._params_for(spec, flags | (Z.ZP_UPDATE_GLOBAL if fused else 0))
     pool = Z.make_pool(wl.k_pool, wl.v_pool)
     batch = Z.DeviceBatch(
         slot=torch.from_numpy(wl.slots).to(dev),
@@ -344,7 +345,7 @@ def _full_size_sampled(spec, n_samples, seed, fused=False):
         num_slots=R, n_cap=wl.n_cap)
     out = Z.alloc_outputs(U, k, wl.n_cap, dev, debug=True)
     ws = Z.alloc_workspace(pool, zparams, R, dev)
-    _say(f"[full] compress {spec.name}: U={U}")
+    _say(f"[full] compress {spec.name}: U={U} flags={flags} workspace={ws.numel() * ws.element_size()} B")
     Z.zp_compress(pool, batch, wl.q_window, wl.global_scores, zparams, out, ws)
     if not fused:
         Z.zp_update_global(wl.global_scores, pool, batch, out, zparams)
@@ -364,6 +365,11 @@ def test_full_size_small_model_sampled():
 def test_full_size_8b_sampled():
     # the timed launch: global update inside the compression kernel
     _full_size_sampled(synth.EIGHT_B, 6, 12, fused=True)
+
+
+def test_full_size_8b_split_sampled():
+    # the same batch on the split-unit schedule (bench.py --split-units)
+    _full_size_sampled(synth.EIGHT_B, 6, 14, fused=True, flags=Z.ZP_SPLIT_UNITS)
 
 
 def test_full_size_prefix_sampled():
