@@ -607,7 +607,7 @@ def _random_case(seed):
                   max_blocks=n_max + 3)
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(48))
 def test_random_shapes(seed):
     case = _random_case(seed)
     _check(case, f"random shape {seed}, flags {case.flags}")
@@ -643,7 +643,7 @@ def _random_prefix_case(seed):
                   max_blocks=n_max + 3, use_block_manager=True)
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(36))
 def test_random_prefix_shapes(seed):
     case = _random_prefix_case(seed)
     s = case.spec
@@ -696,7 +696,7 @@ def _random_wide_case(seed):
                   max_blocks=n_max + 6, use_block_manager=prefix)
 
 
-@pytest.mark.parametrize("seed", range(10))
+@pytest.mark.parametrize("seed", range(30))
 def test_random_wide_shapes(seed):
     case = _random_wide_case(seed)
     s = case.spec

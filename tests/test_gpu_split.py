@@ -223,7 +223,7 @@ def _random_split_case(seed):
                   max_blocks=n_max + 6, use_block_manager=prefix)
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(48))
 def test_random_split_shapes(seed):
     case = _random_split_case(seed)
     s = case.spec
