@@ -213,7 +213,10 @@ zp_status zp_compress_workspace_bytes(const zp_kv_pool* pool,
  * them and wait until the bounded wait ends with ZP_ESYNC). Both give the same keep sets and bytes; attention values may differ
  * in the last bits (summation order). The split schedule's waits on other
  * workgroups are bounded: if one ever passes its limit (a few seconds), the
- * kernel stops and the workspace error word becomes ZP_ESYNC.
+ * kernel stops and the workspace error word becomes ZP_ESYNC. The
+ * environment variable ZP_SPLIT_SPIN_LIMIT, read at each call, lowers that
+ * limit to the given number of polls (0 to 4194304; other values are
+ * ignored); it exists to exercise the ZP_ESYNC path.
  * Errors: ZP_EINVAL, ZP_EUNSUPPORTED (head_dim not 64/128, block_size not 16,
  * w*G > 192 -- 64 for fp32 with head_dim 128 --, n_cap > 16384, or, for fp32
  * with head_dim 128 only, n_cap above about 6100: the per-token scores of a
@@ -235,7 +238,8 @@ zp_status zp_update_global(float* global_scores, const zp_kv_pool* pool,
 
 /* Reads the device error word of a workspace after the caller's stream work
  * has finished: synchronises `stream`, stores ZP_OK, ZP_EDEVICE or ZP_ESYNC
- * in *code and clears the word. Errors: ZP_EINVAL, ZP_EHIP. */
+ * in *code and clears the word. A call that met both a bad table entry and a
+ * wait past its limit reports either one. Errors: ZP_EINVAL, ZP_EHIP. */
 zp_status zp_workspace_error(void* workspace, void* stream, int32_t* code);
 
 /* Decode attention over a paged cache, the consumer of the compressed blocks

@@ -254,7 +254,9 @@ zp_status zp_workspace_error(void* workspace, void* stream, int32_t* code) {
   e = hipMemcpyAsync(workspace, &zero, sizeof(zero), hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return fail(ZP_EHIP, "zp_workspace_error: %s", hipGetErrorString(e));
-  *code = word == 0 ? ZP_OK : ZP_EDEVICE;
+  // the kernels store ZP_EDEVICE or ZP_ESYNC; any other nonzero word is
+  // reported as ZP_EDEVICE
+  *code = word == 0 ? ZP_OK : word == ZP_ESYNC ? ZP_ESYNC : ZP_EDEVICE;
   return ZP_OK;
 }
 

@@ -54,6 +54,7 @@
 // records ZP_ESYNC and every workgroup returns.
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
 #include <type_traits>
 
 #include "zp_device.h"
@@ -74,7 +75,7 @@ constexpr int kMaxParts = 8;
 constexpr int kMaxGroups = 256;
 constexpr int kMaxRows = 192;
 constexpr int kMaxSlice = 512;
-constexpr int kSpinLimit = 1 << 22;  // polls of one wait (each >= ~0.1 us)
+constexpr int kSpinLimit = 1 << 22;  // default polls of one wait (each >= ~0.1 us)
 constexpr uint32_t kTagBits = 18;    // candidate words: key 32 | pos 14 | tag 18
 constexpr uint32_t kTagMask = (1u << kTagBits) - 1u;
 
@@ -107,6 +108,7 @@ struct SplitArgs {
   char* ws;
   int32_t L, NB, Hkv, Hq, G, w, wG, n_cap, num_slots, max_blocks, n_max, k;
   int32_t P, units, groups;
+  int32_t spin_limit;  // polls of one wait before the call gives up
   uint32_t flags;
   float w_attn, w_global, w_red, sl2;
 };
@@ -122,13 +124,13 @@ __device__ __forceinline__ uint32_t xload32(const uint32_t* p) {
 }
 
 // Polls until ready() holds in every lane of the wave (ready() loads what it
-// still lacks). Returns false once the wait limit is passed or another
+// still lacks). Returns false once `limit` polls found it unready or another
 // workgroup raised the abort flag; then the flag is raised here too.
 template <typename F>
-__device__ __forceinline__ bool wave_poll(F&& ready, uint32_t* abort_flag) {
+__device__ __forceinline__ bool wave_poll(F&& ready, uint32_t* abort_flag, int limit) {
   for (int it = 0;; ++it) {
     if (__all(ready())) return true;
-    if (it >= kSpinLimit || xload32(abort_flag) != 0u) {
+    if (it >= limit || xload32(abort_flag) != 0u) {
       __hip_atomic_store(abort_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return false;
     }
@@ -523,7 +525,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
           all &= have[e];
         }
         return all;
-      }, abort_flag);
+      }, abort_flag, a.spin_limit);
 #pragma unroll
       for (int e = 0; e < kPer; ++e) {
         const int idx = tid + e * kThreads;
@@ -703,8 +705,8 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
     int c_p;
     const int cidx = wg_exclusive_scan(cand ? 1 : 0, scratch, &c_p);
     // in place, this slice's V rows (and, above, its global scores) are read
-    // before any part can hold all candidates and start writing (the next
-    // unit's key loads, issued after the V loads, may stay in flight)
+    // before any part can hold all candidates and start writing; this also
+    // waits for the next unit's table reads, issued after the V loads
     wait_vm0();
     lds_barrier();
     if (cand)
@@ -750,7 +752,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
           all &= have[e];
         }
         return all;
-      }, abort_flag);
+      }, abort_flag, a.spin_limit);
       if (wg_or(!ok, scratch)) {
         if (tid == 0) *a.err = ZP_ESYNC;
         return;
@@ -917,6 +919,18 @@ int split_parts(const zp::CompressGeom& g) {
   return (g.n_cap + slice - 1) / slice;
 }
 
+// Polls of one exchange wait: kSpinLimit, or ZP_SPLIT_SPIN_LIMIT from the
+// environment (read at each call, 0..kSpinLimit) so that a test can make the
+// waits give up and see the call report ZP_ESYNC with every workgroup exited.
+int spin_limit() {
+  const char* e = std::getenv("ZP_SPLIT_SPIN_LIMIT");
+  if (!e || !*e) return kSpinLimit;
+  char* end = nullptr;
+  const long v = std::strtol(e, &end, 10);
+  if (*end != '\0' || v < 0 || v > kSpinLimit) return kSpinLimit;
+  return static_cast<int>(v);
+}
+
 // one workgroup per CU, whole groups of P, at most one group per unit
 int split_groups(const zp::CompressGeom& g) {
   const int P = split_parts(g);
@@ -990,6 +1004,7 @@ zp_status launch_compress_split(const CompressGeom& g, const zp_kv_pool& pool,
   a.P = split_parts(g);
   a.units = g.R * g.L * g.Hkv;
   a.groups = split_groups(g);
+  a.spin_limit = spin_limit();
   if (g.wG <= 128) {
     if (g.d == 128) return launch_split_t<128, 1>(a, stream);
     return launch_split_t<64, 1>(a, stream);

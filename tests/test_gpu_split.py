@@ -230,3 +230,48 @@ def test_random_split_shapes(seed):
     _check(case, f"random split shape {seed}: n_max {s.n_max}, d {s.head_dim}, "
                  f"G {s.q_heads // s.kv_heads}, w {s.window}, S {s.shared_blocks}, "
                  f"n {case.n_tokens}")
+
+
+def test_wait_limit_reports_esync_and_the_workspace_recovers(monkeypatch):
+    """With the exchange waits limited to zero polls (ZP_SPLIT_SPIN_LIMIT=0,
+    read by the host at each call), a workgroup that finds a partner's words
+    missing gives up at once, raises the abort flag and returns; every other
+    workgroup returns at its next unready wait. The call ends normally with
+    ZP_ESYNC in the error word. The same workspace then serves a call at the
+    default limit, whose results equal those of a fresh workspace bit for bit."""
+    spec = synth.scaled(FULL, requests=4, layers=2, pool_blocks=4 * 256 + 8)
+    case = P.Case(spec)
+    wl, glob, host, dev, tables, dst, pinned, n_tok, _ = P.build_inputs(case)
+    R, L, H = spec.requests, spec.layers, spec.kv_heads
+    U, k = R * L * H, spec.keep
+    zparams, _ = P._params_for(spec, SPLIT)
+    shared_ws = None
+
+    def run(limit, ws=None):
+        kp, vp, g = wl.k_pool.clone(), wl.v_pool.clone(), glob.clone()
+        pool = Z.make_pool(kp, vp)
+        out = Z.alloc_outputs(U, k, dev.n_cap, "cuda")
+        ws = ws if ws is not None else Z.alloc_workspace(pool, zparams, R, "cuda")
+        if limit is None:
+            monkeypatch.delenv("ZP_SPLIT_SPIN_LIMIT", raising=False)
+        else:
+            monkeypatch.setenv("ZP_SPLIT_SPIN_LIMIT", str(limit))
+        Z.zp_compress(pool, dev, wl.q_window, g, zparams, out, ws)
+        torch.cuda.synchronize()
+        return Z.zp_workspace_error(ws), ws, (kp, vp, out.keep_idx)
+
+    seen = []
+    for attempt in range(3):
+        err, shared_ws, _ = run(0, shared_ws)
+        seen.append(err)
+        _say(f"[split] zero-poll wait limit, attempt {attempt}: status {err}")
+        assert err in (Z.ZP_ESYNC, Z.ZP_OK)
+        if err == Z.ZP_ESYNC:
+            break
+    assert Z.ZP_ESYNC in seen, f"no wait gave up: {seen}"
+    err1, _, (k1, v1, keep1) = run(None, shared_ws)
+    err2, _, (k2, v2, keep2) = run(None)
+    assert err1 == Z.ZP_OK and err2 == Z.ZP_OK
+    assert torch.equal(keep1, keep2)
+    assert torch.equal(k1, k2) and torch.equal(v1, v2)
+    _say("[split] ZP_ESYNC reported; the workspace serves the next call unchanged")
