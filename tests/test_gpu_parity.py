@@ -126,16 +126,18 @@ def test_prefix_targets_with_block_manager():
            "shared prefix -> target blocks (plans from zp_bm)")
 
 
-def test_device_table_errors_reject_only_their_units():
+@pytest.mark.parametrize("flags", [0, Z.ZP_SPLIT_UNITS], ids=["one-workgroup", "split-units"])
+def test_device_table_errors_reject_only_their_units(flags):
     """A block id outside the pool (request 1) and a token count below the
     trigger (request 2) are caught by the kernel: those units write only
     their markers (keep row starting with -1, first hole -1), the error word
     reads ZP_EDEVICE, the global update skips them, and request 0 is
-    compressed as usual."""
+    compressed as usual. On the split-unit schedule every part of a unit
+    checks the whole table, so all of them skip it without an exchange."""
     spec = synth.scaled(EIGHT_B, requests=3)
     case = P.Case(spec)
     wl, glob, host, dev, tables, dst, pinned, n_tok, _ = P.build_inputs(case)
-    zparams, oparams = P._params_for(spec, 0)
+    zparams, oparams = P._params_for(spec, flags)
     pool = Z.make_pool(wl.k_pool, wl.v_pool)
     R, L, H, b = spec.requests, spec.layers, spec.kv_heads, spec.block_size
     U, k, n = R * L * H, spec.keep, spec.n_tokens
