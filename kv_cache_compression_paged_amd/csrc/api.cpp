@@ -464,6 +464,7 @@ const char* zp_status_str(zp_status s) {
     case ZP_ENOSPACE: return "ZP_ENOSPACE";
     case ZP_EHIP: return "ZP_EHIP";
     case ZP_EDEVICE: return "ZP_EDEVICE";
+    case ZP_ESYNC: return "ZP_ESYNC";
     default: return "ZP_UNKNOWN";
   }
 }

@@ -11,6 +11,7 @@ import ctypes
 import os
 import re
 import subprocess
+from pathlib import Path
 
 import numpy as np
 import pytest
@@ -45,8 +46,23 @@ def test_status_strings():
     lib = Z.lib()
     for code, name in [(0, "ZP_OK"), (-1, "ZP_EINVAL"), (-2, "ZP_EUNSUPPORTED"),
                        (-3, "ZP_EWORKSPACE"), (-4, "ZP_ENOSPACE"), (-5, "ZP_EHIP"),
-                       (-6, "ZP_EDEVICE")]:
+                       (-6, "ZP_EDEVICE"), (-7, "ZP_ESYNC")]:
         assert lib.zp_status_str(code).decode() == name
+    assert lib.zp_status_str(-99).decode() == "ZP_UNKNOWN"
+
+
+def test_every_declared_status_has_its_name_everywhere():
+    """Each ZP_OK / ZP_E* code the header defines is named by zp_status_str
+    and by the binding, and the binding's constant has the header's value."""
+    header = (Path(__file__).resolve().parents[1] / "include" / "zipage.h").read_text()
+    codes = {m.group(1): int(m.group(2)) for m in
+             re.finditer(r"#define (ZP_(?:OK|E[A-Z]+))\s+(-?\d+)", header)}
+    assert len(codes) >= 8 and codes["ZP_OK"] == 0
+    lib = Z.lib()
+    for name, code in codes.items():
+        assert lib.zp_status_str(code).decode() == name
+        assert getattr(Z, name) == code
+        assert Z._status_name(code) == name
 
 
 # ------------------------------------------------------- block manager ---
