@@ -210,8 +210,9 @@ zp_status zp_compress_workspace_bytes(const zp_kv_pool* pool,
  * workspace, and every K/V row is read once. Its grid holds one workgroup
  * per CU and the workgroups of a unit wait on each other, so two such calls
  * must not run concurrently on one device (they could hold every CU between
- * them and wait until the bounded wait ends with ZP_ESYNC). Both give the same keep sets and bytes; attention values may differ
- * in the last bits (summation order). The split schedule's waits on other
+ * them and wait until the bounded wait ends with ZP_ESYNC). Both schedules
+ * give the same keep sets and bytes; attention values may differ in the last
+ * bits (summation order). The split schedule's waits on other
  * workgroups are bounded: if one ever passes its limit (a few seconds), the
  * kernel stops and the workspace error word becomes ZP_ESYNC. The
  * environment variable ZP_SPLIT_SPIN_LIMIT, read at each call, lowers that
