@@ -61,12 +61,16 @@ def _linear_to_ring(q_window, seq, slots, w):
     return ring
 
 
-@pytest.mark.parametrize("flags,shift", [(0, 0), (Z.ZP_NONCAUSAL, 0), (0, 16), (0, 37)])
+@pytest.mark.parametrize("flags,shift", [(0, 0), (Z.ZP_NONCAUSAL, 0), (0, 16), (0, 37),
+                                         (Z.ZP_SPLIT_UNITS, 0), (Z.ZP_SPLIT_UNITS, 37)])
 def test_ring_window_compression_is_bit_identical(flags, shift):
     """shift > 0: the sequence is ahead of the cache (earlier compressions
-    evicted tokens), so the ring is indexed by seq_pos, not n."""
+    evicted tokens), so the ring is indexed by seq_pos, not n. With
+    ZP_SPLIT_UNITS the units span 4 slices of 512 tokens, and every part
+    reads the window rows out of the ring itself."""
+    n_max = 100 if flags & Z.ZP_SPLIT_UNITS else 20
     spec = synth.scaled(synth.EIGHT_B, requests=3, layers=2, kv_heads=2, q_heads=8,
-                        n_max=20, pool_blocks=3 * 20 + 3 * 3)
+                        n_max=n_max, pool_blocks=3 * n_max + 3 * 3)
     n = spec.n_tokens
     case = P.Case(spec, n_tokens=[n, n + 7, n + 21], max_blocks=spec.n_max + 2)
     wl, glob, host, dev, tables, dst, pinned, n_tok, _ = P.build_inputs(case)
