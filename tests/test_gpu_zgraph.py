@@ -43,15 +43,19 @@ def _capture(fn):
     return g
 
 
-def test_compress_graph_replays_match_eager():
+@pytest.mark.parametrize("schedule", [0, Z.ZP_SPLIT_UNITS], ids=["one-workgroup", "split-units"])
+def test_compress_graph_replays_match_eager(schedule):
+    # the split-unit schedule records two kernel nodes: the fill kernel that
+    # clears the exchange area, then the persistent kernel (3 slices a unit)
+    n_max = 96 if schedule else 16
     spec = synth.scaled(synth.EIGHT_B, requests=3, layers=2, kv_heads=2, q_heads=8,
-                        n_max=16, pool_blocks=64)
-    _say(f"[graph] compress {spec.name} (scaled)")
+                        n_max=n_max, pool_blocks=3 * n_max + 16)
+    _say(f"[graph] compress {spec.name} (scaled), flags {schedule}")
     wl = synth.make(spec, device=DEV)
     R, L, H = spec.requests, spec.layers, spec.kv_heads
     U = R * L * H
     params = Z.make_params(spec.n_max, spec.window, spec.q_heads, Z.ZP_BF16,
-                           flags=Z.ZP_UPDATE_GLOBAL)
+                           flags=Z.ZP_UPDATE_GLOBAL | schedule)
     pool = Z.make_pool(wl.k_pool, wl.v_pool)
     tables = torch.from_numpy(wl.tables).to(DEV)
     batch = Z.DeviceBatch(slot=torch.from_numpy(wl.slots).to(DEV),
