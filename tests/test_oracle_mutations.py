@@ -97,6 +97,49 @@ def global_without_attention(g, attn, keep, k):
     return out
 
 
+def row_location_ignores_table(table, t, b):
+    return t // b, t % b                  # logical block used as the physical one
+
+
+def pinned_without_prefix(n, n_pinned_blocks, b, w, protect_window):
+    m = np.zeros(n, dtype=bool)
+    if protect_window:
+        m[n - w:] = True
+    return m
+
+
+def pinned_window_one_short(n, n_pinned_blocks, b, w, protect_window):
+    m = np.zeros(n, dtype=bool)
+    m[: n_pinned_blocks * b] = True
+    if protect_window:
+        m[n - w + 1:] = True
+    return m
+
+
+def first_hole_one_late(keep):
+    for t, src in enumerate(keep):
+        if src != t:
+            return t + 1
+    return len(keep)
+
+
+def compact_reversed(src_pool, dst_pool, src_table, dst_table, layer, head, keep, b):
+    k = len(keep)
+    for t, src in enumerate(keep):
+        sb, ss = Z.row_location(src_table, int(src), b)
+        db, ds = Z.row_location(dst_table, k - 1 - t, b)
+        dst_pool[layer, db, head, ds] = src_pool[layer, sb, head, ss]
+
+
+def compact_reads_through_dst_table(src_pool, dst_pool, src_table, dst_table, layer, head,
+                                    keep, b):
+    for t, src in enumerate(keep):
+        sb, ss = Z.row_location(dst_table, int(src) % (len(dst_table) * b), b)
+        db, ds = Z.row_location(dst_table, t, b)
+        if (sb, ss) != (db, ds):
+            dst_pool[layer, db, head, ds] = src_pool[layer, sb, head, ss]
+
+
 @pytest.fixture(autouse=True)
 def _keep_originals():
     Z._orig_window_attention = Z.window_attention
@@ -120,6 +163,13 @@ CASES = [
     ("select_keep", select_ties_reversed, P.test_select_forced_ties_keep_prefix,
      ()),
     ("update_global", global_without_attention, P.test_hand_example_causal, ()),
+    ("row_location", row_location_ignores_table, P.test_gather_rows_follows_block_table, ()),
+    ("pinned_mask", pinned_without_prefix, P.test_pinned_mask_and_hole, ()),
+    ("pinned_mask", pinned_window_one_short, P.test_pinned_mask_and_hole, ()),
+    ("first_hole", first_hole_one_late, P.test_pinned_mask_and_hole, ()),
+    ("compact_unit", compact_reversed, P.test_hand_example_compaction_bytes, ()),
+    ("compact_unit", compact_reads_through_dst_table,
+     P.test_compress_into_target_blocks_after_a_shared_prefix, ()),
 ]
 
 

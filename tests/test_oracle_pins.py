@@ -363,6 +363,52 @@ def test_compress_moves_exact_bytes_in_place(extra):
             assert out["pool_k"][idx].tobytes() == pool_k[idx].tobytes()
 
 
+
+def test_compress_into_target_blocks_after_a_shared_prefix():
+    """With S leading shared blocks the kept private rows go, in order, to
+    fresh target blocks listed after the prefix in the destination table
+    ([zh §2.2]): each target row is a byte copy of its source row read through
+    the source table, the shared blocks and every source block keep their
+    bytes, and the S*b prefix tokens are kept where they are."""
+    rng = np.random.default_rng(31)
+    R, L, H, G, d, b, n_max, w, S = 2, 2, 2, 2, 8, 4, 5, 3, 2
+    private = n_max - S
+    nb = S + R * private + R * (n_max - 1 - S) + 2
+    pool_k = rng.standard_normal((L, nb, H, b, d)).astype(np.float32)
+    pool_v = rng.standard_normal((L, nb, H, b, d)).astype(np.float32)
+    perm = rng.permutation(nb)
+    shared = perm[:S]
+    src = np.stack([np.concatenate([shared, perm[S + r * private:S + (r + 1) * private]])
+                    for r in range(R)])
+    base = S + R * private
+    fresh = [perm[base + r * (n_max - 1 - S):base + (r + 1) * (n_max - 1 - S)]
+             for r in range(R)]
+    dst = np.stack([np.concatenate([shared, fresh[r], [shared[0]]]) for r in range(R)])
+    q = rng.standard_normal((R, L, w, H * G, d)).astype(np.float32)
+    glob = rng.random((R, L, H, n_max * b)).astype(np.float32)
+    batch = O.Batch(slots=np.arange(R), n_tokens=np.full(R, n_max * b), src_tables=src,
+                    dst_tables=dst, n_pinned=np.full(R, S))
+    p = O.Params(n_max=n_max, block_size=b, window=w)
+    out = O.compress(pool_k, pool_v, "f32", q, "f32", glob, batch, p)
+    k = p.keep_tokens
+    targets = set()
+    for (r, l, h), res in out["units"].items():
+        assert len(res.keep) == k
+        assert list(res.keep[:S * b]) == list(range(S * b))
+        for t in range(S * b, k):
+            sblk, sslot = src[r][res.keep[t] // b], res.keep[t] % b
+            dblk, dslot = dst[r][t // b], t % b
+            assert dblk in fresh[r]
+            assert out["pool_k"][l, dblk, h, dslot].tobytes() == \
+                pool_k[l, sblk, h, sslot].tobytes()
+            assert out["pool_v"][l, dblk, h, dslot].tobytes() == \
+                pool_v[l, sblk, h, sslot].tobytes()
+        targets.update(int(x) for x in fresh[r])
+    for blk in range(nb):
+        if blk not in targets:
+            assert out["pool_k"][:, blk].tobytes() == pool_k[:, blk].tobytes()
+            assert out["pool_v"][:, blk].tobytes() == pool_v[:, blk].tobytes()
+
 # ----------------------------------------------------------- bookkeeping ---
 
 def test_block_pool_lifo_and_plans():
