@@ -42,6 +42,19 @@ def test_library_exports_every_declared_symbol():
     assert set(Z.EXPORTED) == set(declared)
 
 
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without the built library every entry point raises before doing any
+    work: there is no fallback path."""
+    monkeypatch.setattr(Z, "_lib", None)
+    monkeypatch.setattr(Z, "LIB_PATH", str(tmp_path / "libzipage.so"))
+    with pytest.raises(Z.ZipageError) as ei:
+        Z.lib()
+    assert ei.value.status == Z.ZP_EHIP and "not built" in str(ei.value)
+    with pytest.raises(Z.ZipageError):
+        Z.zp_compress_workspace_bytes(Z.KVPool(), Z.Params(), 1)
+    with pytest.raises(Z.ZipageError):
+        Z.BlockManager(8)
+
 def test_status_strings():
     lib = Z.lib()
     for code, name in [(0, "ZP_OK"), (-1, "ZP_EINVAL"), (-2, "ZP_EUNSUPPORTED"),
