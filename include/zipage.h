@@ -121,7 +121,11 @@ typedef struct {
 /* The requests of one compression call (R = num_reqs). Device arrays:
  *   slot[R]        -- query-slot row of each request: selects its window in
  *                     q_window and its row of global scores ([zh] §2.2: only
- *                     requests holding a query slot are compressed).
+ *                     requests holding a query slot are compressed). The
+ *                     entries are distinct within a call: the kernels reject
+ *                     every request whose slot another request of the call
+ *                     also names, as a bad table entry (ZP_EDEVICE; for
+ *                     zp_update_global: such units are left alone).
  *   n_tokens[R]    -- tokens held, n; must satisfy n_max*b <= n <= n_cap and
  *                     ceil(n/b) <= max_blocks (n > n_max*b: prefill overshoot).
  *   src_table[R][max_blocks] -- current block table (logical -> physical).
@@ -133,6 +137,12 @@ typedef struct {
  *                     source block, entry n_max-1 is any block (the new tail).
  *   n_pinned[R]    -- S, the leading shared blocks, kept whole and never
  *                     written ([zh] §2.2, [de] §2, [fr] §2.C).
+ *                     The blocks a request writes -- src_table entries
+ *                     [S, ceil(n/b)) when it compacts in place, dst_table
+ *                     entries [S, n_max-1) when it writes targets -- belong
+ *                     to that request alone: no other request of the call
+ *                     reads or writes them (zp_bm_plan_compress guarantees
+ *                     it; the kernels do not check it).
  *   seq_pos[R]     -- optional (NULL: n_tokens), read with ZP_WINDOW_RING
  *                     only: sequence position P of the request's next token,
  *                     the position zp_capture_queries rings by. Window row i
@@ -361,9 +371,14 @@ int32_t zp_bm_free_list(const zp_bm* bm, int32_t* ids, int32_t cap);
  * Blocks that compression frees (old private blocks S..n_max-2 when S > 0,
  * then every block past n_max) are recorded in the plan, in logical order,
  * and pushed only by zp_bm_commit. Outputs dst_tables[R][n_max] and
- * n_pinned[R] (= S) on the host. Errors: ZP_EINVAL (bad sizes, n_tokens
- * below n_max*b, a block id out of range), ZP_ENOSPACE (not enough free
- * blocks for the targets: nothing changed). */
+ * n_pinned[R] (= S) on the host. Every block a request holds after its
+ * shared run ([S, ceil(n/b))) is rewritten in place, kept as the tail or
+ * freed, so it must have refcount 1 and appear once in the whole call
+ * ([de] §2: blocks with a count above one stay intact).
+ * Errors: ZP_EINVAL (bad sizes, n_tokens below n_max*b, a block id out of
+ * range, a block after the shared run with refcount other than 1 or listed
+ * twice), ZP_ENOSPACE (not enough free blocks for the targets). On an error
+ * nothing changed and *plan is NULL. */
 zp_status zp_bm_plan_compress(zp_bm* bm, int32_t num_reqs,
                               const int32_t* host_tables, int32_t max_blocks,
                               const int32_t* n_tokens, int32_t n_max,

@@ -117,6 +117,7 @@ zp_status zp_bm_plan_compress(zp_bm* bm, int32_t num_reqs,
   *plan = nullptr;
   const int32_t nb = static_cast<int32_t>(bm->refcount.size());
   std::vector<int32_t> shared(num_reqs);
+  std::vector<char> mark(nb, 0);
   int64_t need = 0;
   for (int32_t r = 0; r < num_reqs; ++r) {
     const int64_t n = n_tokens[r];
@@ -133,6 +134,19 @@ zp_status zp_bm_plan_compress(zp_bm* bm, int32_t num_reqs,
                         static_cast<long long>(j), t[j]);
     int32_t s = 0;
     while (s < n_max - 1 && bm->refcount[t[s]] > 1) ++s;
+    // every block past the shared run is written in place, becomes the tail
+    // or is freed: it must belong to this request alone, once
+    for (int64_t j = s; j < held; ++j) {
+      if (bm->refcount[t[j]] != 1)
+        return zp::fail(ZP_EINVAL, "zp_bm_plan_compress: request %d block %lld "
+                        "(id %d) has refcount %d; blocks after the shared "
+                        "prefix must be held by one request", r,
+                        static_cast<long long>(j), t[j], bm->refcount[t[j]]);
+      if (mark[t[j]])
+        return zp::fail(ZP_EINVAL, "zp_bm_plan_compress: block id %d appears "
+                        "twice among the private blocks of the call", t[j]);
+      mark[t[j]] = 1;
+    }
     shared[r] = s;
     if (s > 0) need += n_max - 1 - s;
   }

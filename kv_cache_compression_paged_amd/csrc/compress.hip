@@ -77,7 +77,7 @@ struct ScoreArgs {
   float* score;
   int32_t* hole_out;
   int32_t* err;
-  int32_t L, NB, Hkv, Hq, G, w, wG, n_cap, num_slots, max_blocks, n_max, k;
+  int32_t R, L, NB, Hkv, Hq, G, w, wG, n_cap, num_slots, max_blocks, n_max, k;
   uint32_t flags;
   float w_attn, w_global, w_red, sl2;  // sl2 = softmax scale * log2(e)
 };
@@ -196,6 +196,8 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(ScoreArgs a) {
     }
     for (int j = tid; j < a.n_max; j += kThreads)
       bad |= dst_tab[j] < 0 || dst_tab[j] >= a.NB;
+    // a slot names one global-score row, rewritten in place by its request
+    for (int j = tid; j < a.R; j += kThreads) bad |= j != r && a.slot[j] == slot;
   }
   if (__syncthreads_or(bad)) {
     if (tid == 0) {  // markers of a rejected unit; nothing else is written
@@ -941,6 +943,7 @@ zp_status launch_compress(const CompressGeom& g, const zp_kv_pool& pool,
   a.score = out.score;
   a.hole_out = out.first_hole;
   a.err = err;
+  a.R = g.R;
   a.L = g.L;
   a.NB = g.num_blocks;
   a.Hkv = g.Hkv;

@@ -106,7 +106,7 @@ struct SplitArgs {
   int32_t* hole_out;
   int32_t* err;
   char* ws;
-  int32_t L, NB, Hkv, Hq, G, w, wG, n_cap, num_slots, max_blocks, n_max, k;
+  int32_t R, L, NB, Hkv, Hq, G, w, wG, n_cap, num_slots, max_blocks, n_max, k;
   int32_t P, units, groups;
   int32_t spin_limit;  // polls of one wait before the call gives up
   uint32_t flags;
@@ -346,6 +346,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
         bad |= b < 0 || b >= a.NB;
         dtab[j] = b;
       }
+      for (int j = tid; j < a.R; j += kThreads) bad |= j != r && a.slot[j] == slot;
     }
     for (int j = tid; j < SLICE; j += kThreads) dest_l[j] = 0;
     if (wg_or(bad, scratch)) {
@@ -984,6 +985,7 @@ zp_status launch_compress_split(const CompressGeom& g, const zp_kv_pool& pool,
   a.hole_out = out.first_hole;
   a.err = static_cast<int32_t*>(workspace);
   a.ws = static_cast<char*>(workspace);
+  a.R = g.R;
   a.L = g.L;
   a.NB = g.num_blocks;
   a.Hkv = g.Hkv;

@@ -21,7 +21,7 @@ struct GlobalArgs {
   const float* attn;
   const int32_t* slot;
   const int32_t* n_tokens;
-  int32_t L, Hkv, n_cap, num_slots, n_max, k;
+  int32_t R, L, Hkv, n_cap, num_slots, n_max, k;
 };
 
 __global__ __launch_bounds__(kThreads) void global_kernel(GlobalArgs a) {
@@ -38,6 +38,8 @@ __global__ __launch_bounds__(kThreads) void global_kernel(GlobalArgs a) {
   float* g = a.glob + (static_cast<int64_t>(slot) * a.L * a.Hkv + l * a.Hkv + h) * a.n_cap;
   bool bad = false;
   for (int t = threadIdx.x; t < a.k; t += kThreads) bad |= keep[t] < 0 || keep[t] >= n;
+  // two requests naming one slot would rewrite one row together: skip both
+  for (int j = threadIdx.x; j < a.R; j += kThreads) bad |= j != r && a.slot[j] == slot;
   if (__syncthreads_or(bad)) return;
   for (int t = threadIdx.x; t < a.n_cap; t += kThreads) row[t] = g[t];
   __syncthreads();
@@ -64,6 +66,7 @@ zp_status launch_global(const CompressGeom& g, float* global_scores,
   a.attn = attn;
   a.slot = batch.slot;
   a.n_tokens = batch.n_tokens;
+  a.R = g.R;
   a.L = g.L;
   a.Hkv = g.Hkv;
   a.n_cap = g.n_cap;

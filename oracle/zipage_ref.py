@@ -485,6 +485,22 @@ class BlockPool:
             s += 1
         return s
 
+    def check_private(self, tables, n_tokens, shared, b: int) -> None:
+        """Blocks a request holds after its shared run are rewritten in place,
+        kept as its tail or freed, so no other request may hold them: each
+        must have a count of one and appear once in the call ([de §2]: blocks
+        with a count above one stay intact; [zh §2.2]: shared data is never
+        moved)."""
+        private = set()
+        for r in range(len(tables)):
+            held = (int(n_tokens[r]) + b - 1) // b
+            for bid in tables[r][shared[r]:held]:
+                bid = int(bid)
+                if self.refcount[bid] != 1 or bid in private:
+                    raise ValueError(f"block {bid} after the shared prefix is "
+                                     "shared or listed twice")
+                private.add(bid)
+
     def plan_compress(self, tables: Sequence[Sequence[int]],
                       n_tokens: Sequence[int], n_max: int, b: int) -> Plan:
         """Plan one compression call; no state changes until commit, except
@@ -513,6 +529,7 @@ class BlockPool:
             shared.append(sb)
             if sb > 0:
                 need += n_max - 1 - sb
+        self.check_private(tables, n_tokens, shared, b)
         if need > len(self.stack):
             raise MemoryError("free list exhausted")
         plan = Plan(dst_tables=dst, n_pinned=pinned)

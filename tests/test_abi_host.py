@@ -164,6 +164,40 @@ def test_block_manager_errors_change_nothing():
     assert bm.free_count() == 6
 
 
+def test_block_manager_rejects_shared_or_repeated_private_blocks():
+    """The library planner refuses what the oracle's refuses (a block after
+    the shared run with another holder, or listed twice in the call), with
+    ZP_EINVAL and no state change."""
+    bm, bp = Z.BlockManager(16), O.BlockPool(16)
+    sh = bm.alloc(2)
+    assert sh == bp.alloc(2)
+    for x in sh:
+        bm.incref(x)
+        bp.incref(x)
+    r0 = bm.alloc(4)
+    assert r0 == bp.alloc(4)
+    r1 = sh + bm.alloc(2)
+    assert r1[2:] == bp.alloc(2)
+    cases = [
+        ([[r0[0], sh[1], r0[2], r0[3]]], [8]),
+        ([r0, [r0[0]] + r1[1:]], [8, 8]),
+        ([r1, [r1[0], r1[1], r1[2], r0[3]], r0], [8, 8, 8]),
+        ([r0 + [sh[0]]], [9]),
+    ]
+    for tabs, ntok in cases:
+        width = max(len(t) for t in tabs)
+        arr = np.array([t + [0] * (width - len(t)) for t in tabs], dtype=np.int32)
+        with pytest.raises(ValueError):
+            bp.plan_compress(tabs, ntok, n_max=4, b=2)
+        with pytest.raises(Z.ZipageError) as ei:
+            bm.plan_compress(arr, ntok, 4, 2)
+        assert ei.value.status == Z.ZP_EINVAL
+        _same_state(bm, bp)
+    plan = bm.plan_compress(np.array([r0, r1], dtype=np.int32), [8, 8], 4, 2)
+    assert plan.n_pinned.tolist() == [0, 2]
+    bm.abort(plan)
+
+
 # ------------------------------------------------ argument validation ---
 
 FAKE = 0x10000  # never dereferenced: every call below fails validation first

@@ -185,6 +185,71 @@ def test_device_table_errors_reject_only_their_units(flags):
         assert nv[:k].tobytes() == vr[keep[u]].tobytes()
 
 
+@pytest.mark.parametrize("flags", [0, Z.ZP_SPLIT_UNITS, Z.ZP_UPDATE_GLOBAL,
+                                   Z.ZP_SPLIT_UNITS | Z.ZP_UPDATE_GLOBAL],
+                         ids=["one-workgroup", "split-units", "fused-update",
+                              "split-fused-update"])
+def test_duplicate_slots_are_rejected(flags):
+    """Requests 1 and 3 name the same query slot, so both would rewrite one
+    global-score row: every unit of both is rejected (markers only, error
+    word ZP_EDEVICE, pools and global rows untouched, the separate global
+    update skips them too), while requests 0 and 2 compress as usual."""
+    spec = synth.scaled(EIGHT_B, requests=4, pool_blocks=4 * EIGHT_B.n_max + 8)
+    case = P.Case(spec)
+    wl, glob, host, dev, tables, dst, pinned, n_tok, _ = P.build_inputs(case)
+    zparams, oparams = P._params_for(spec, flags)
+    pool = Z.make_pool(wl.k_pool, wl.v_pool)
+    R, L, H, b = spec.requests, spec.layers, spec.kv_heads, spec.block_size
+    U, k, n = R * L * H, spec.keep, spec.n_tokens
+    dev.slot[3] = dev.slot[1]
+    out = Z.alloc_outputs(U, k, dev.n_cap, "cuda", debug=True)
+    out.keep_idx.fill_(-7)
+    ws = Z.alloc_workspace(pool, zparams, R, "cuda")
+    k_before, v_before, g_before = wl.k_pool.clone(), wl.v_pool.clone(), glob.clone()
+    Z.zp_compress(pool, dev, wl.q_window, glob, zparams, out, ws)
+    if not flags & Z.ZP_UPDATE_GLOBAL:
+        Z.zp_update_global(glob, pool, dev, out, zparams)
+    torch.cuda.synchronize()
+    assert Z.zp_workspace_error(ws) == Z.ZP_EDEVICE
+    per_req = L * H
+    for r in (1, 3):
+        rows = slice(r * per_req, (r + 1) * per_req)
+        assert bool((out.keep_idx[rows, 0] == -1).all())
+        assert bool((out.keep_idx[rows, 1:] == -7).all())
+        assert bool((out.first_hole[rows] == -1).all())
+        blocks = torch.from_numpy(tables[r]).cuda().long()
+        assert torch.equal(wl.k_pool[:, blocks], k_before[:, blocks])
+        assert torch.equal(wl.v_pool[:, blocks], v_before[:, blocks])
+    assert torch.equal(glob[1], g_before[1])   # the shared row (slot 1)
+    assert torch.equal(glob[3], g_before[3])   # slot 3: named by no request now
+    keep = out.keep_idx.cpu().numpy()
+    attn = out.attn.cpu().numpy().astype(np.float64)
+    g_now = glob.cpu().numpy()
+    for r in (0, 2):
+        blocks = torch.from_numpy(tables[r]).cuda().long()
+        for l in range(L):
+            for h in range(H):
+                u = (r * L + l) * H + h
+                kr = O.gather_rows(host["k"], tables[r], l, h, n, b)
+                vr = O.gather_rows(host["v"], tables[r], l, h, n, b)
+                G = spec.q_heads // H
+                q = O.widen(host["q"][r, l, :, h * G:(h + 1) * G], spec.dtype)
+                g0 = host["g"][r, l, h].astype(np.float64)
+                ur = O.score_unit(q, O.widen(kr, spec.dtype), g0, n, 0, oparams)
+                assert np.all(np.abs(attn[u, :n] - ur.attn) <=
+                              P.ATTN_RTOL * np.abs(ur.attn) + P.ATTN_ATOL)
+                diff = set(keep[u].tolist()) ^ set(ur.keep.tolist())
+                fin = np.isfinite(ur.score)
+                tau = min(float(ur.score[t]) for t in ur.keep if fin[t])
+                assert all(abs(ur.score[t] - tau) <= P.BAND for t in diff)
+                nk = synth.raw_numpy(wl.k_pool[l, blocks, h].reshape(n, -1))
+                nv = synth.raw_numpy(wl.v_pool[l, blocks, h].reshape(n, -1))
+                assert nk[:k].tobytes() == kr[keep[u]].tobytes()
+                assert nv[:k].tobytes() == vr[keep[u]].tobytes()
+                gref = O.update_global(host["g"][r, l, h], ur.attn, keep[u], k)
+                assert np.all(np.abs(g_now[r, l, h] - gref) <= 1e-4 * np.abs(gref) + 1e-6)
+
+
 def _forced_global(spec, evict_positions):
     g = np.zeros((spec.requests, spec.layers, spec.kv_heads, spec.n_tokens))
     g[..., list(evict_positions)] = -100.0

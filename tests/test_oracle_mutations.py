@@ -181,6 +181,23 @@ def test_planted_mistake_is_caught(name, mutant, pin, args):
         assert _fails(pin, *args), f"{mutant.__name__} slipped past {pin.__name__}"
 
 
+def test_block_pool_without_private_check_is_caught():
+    """A planner that lets a shared or repeated block through after the
+    shared run (it would compact into, or free, another request's block)."""
+    pin = P.test_block_pool_rejects_shared_or_repeated_private_blocks
+
+    def fails():
+        try:
+            pin()
+        except (AssertionError, pytest.fail.Exception):
+            return True
+        return False
+
+    assert not fails()
+    with mock.patch.object(Z.BlockPool, "check_private", lambda *a, **k: None):
+        assert fails()
+
+
 def capture_row_off_by_one(q_window, q, slot, pos, w):
     S = q_window.shape[0]
     for r in range(q.shape[0]):

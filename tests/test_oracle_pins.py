@@ -447,16 +447,43 @@ def test_block_pool_in_place_and_overshoot():
 
 
 def test_block_pool_exhausted_changes_nothing():
-    bp = O.BlockPool(5)
+    bp = O.BlockPool(8)
     sh = bp.alloc(1)
     bp.incref(sh[0])
     r = sh + bp.alloc(3)
-    stack = list(bp.stack)
+    r2 = sh + bp.alloc(3)
     bp.alloc(1)
-    stack = list(bp.stack)
+    stack, refs = list(bp.stack), list(bp.refcount)
     with pytest.raises(MemoryError):
-        bp.plan_compress([r, r], [8, 8], n_max=4, b=2)  # needs 4 targets, 0 free
-    assert bp.stack == stack
+        bp.plan_compress([r, r2], [8, 8], n_max=4, b=2)  # needs 4 targets, 0 free
+    assert bp.stack == stack and bp.refcount == refs
+
+
+def test_block_pool_rejects_shared_or_repeated_private_blocks():
+    """Blocks after the shared run are written, kept as the tail or freed:
+    a block with another holder, or one listed twice in the call, must make
+    the plan fail and leave the pool as it was ([de §2], [zh §2.2])."""
+    bp = O.BlockPool(16)
+    sh = bp.alloc(2)
+    for x in sh:
+        bp.incref(x)
+    r0 = bp.alloc(4)                       # private: [2, 3, 4, 5]
+    r1 = sh + bp.alloc(2)                  # shared prefix of 2, then private
+    state = (list(bp.stack), list(bp.refcount))
+    bad_tables = [
+        [[r0[0], sh[1], r0[2], r0[3]]],    # a shared block after a private one
+        [r0, [r0[0]] + r1[1:]],            # r0[0] held by two requests (S = 0)
+        [r1, [r1[0], r1[1], r1[2], r0[3]], r0],  # r0[3] listed twice
+        [[r0[0], r0[1], r0[2], r0[3], sh[0]]],   # overshoot block is shared
+    ]
+    ntok = [[8], [8, 8], [8, 8, 8], [9]]
+    for tabs, n in zip(bad_tables, ntok):
+        with pytest.raises(ValueError):
+            bp.plan_compress(tabs, n, n_max=4, b=2)
+        assert (list(bp.stack), list(bp.refcount)) == state
+    # the same requests, well formed, plan fine
+    plan = bp.plan_compress([r0, r1], [8, 8], n_max=4, b=2)
+    assert list(plan.n_pinned) == [0, 2]
 
 
 # ---------------------------------------------------------------- decode ---
