@@ -48,6 +48,9 @@ class Case:
     identical_keys: bool = False
     use_block_manager: bool = False               # prefix plans from zp_bm
     outlier: Optional[Tuple[int, float]] = None   # (logical position, scale)
+    weights: Optional[Tuple[float, float, float]] = None  # w_attn, w_global, w_red
+    sm_scale: Optional[float] = None              # None: 1/sqrt(d)
+    small_keys: Optional[float] = None            # scale of 6 rows per 3rd block
 
 
 @dataclass
@@ -62,11 +65,19 @@ class Result:
             self.failures.append(msg)
 
 
-def _params_for(spec: synth.Spec, flags: int) -> Tuple[Z.Params, O.Params]:
+def _params_for(spec: synth.Spec, flags: int,
+                weights: Optional[Tuple[float, float, float]] = None,
+                sm_scale: Optional[float] = None) -> Tuple[Z.Params, O.Params]:
     dt = Z.ZP_BF16 if spec.dtype == "bf16" else Z.ZP_F32
-    zp = Z.make_params(spec.n_max, spec.window, spec.q_heads, dt, flags=flags)
+    # the library receives the weights and the scale as fp32 fields: the
+    # oracle is given those same values
+    wa, wg, wr = (float(np.float32(x)) for x in (weights or (1.0, 0.5, 0.5)))
+    sc = None if sm_scale is None else float(np.float32(sm_scale))
+    zp = Z.make_params(spec.n_max, spec.window, spec.q_heads, dt, w_attn=wa,
+                       w_global=wg, w_red=wr, sm_scale=sc or 0.0, flags=flags)
     op = O.Params(n_max=spec.n_max, block_size=spec.block_size,
-                  window=spec.window,
+                  window=spec.window, w_attn=wa, w_global=wg, w_red=wr,
+                  sm_scale=sc,
                   causal=not (flags & Z.ZP_NONCAUSAL),
                   protect_window=bool(flags & Z.ZP_PROTECT_WINDOW))
     return zp, op
@@ -111,6 +122,13 @@ def build_inputs(case: Case, device: str = "cuda"):
         for r in range(R):
             blk = int(tables[r, pos // b])
             wl.k_pool[:, blk, :, pos % b, :] *= scale
+    if case.small_keys is not None:
+        # rows 0..5 of every third block (all layers and heads) scaled down:
+        # pairs of such keys have |a||c| below the 1e-8 clamp of the cosine
+        # (scale 1e-6), or are zero vectors (scale 0)
+        blocks = sorted(set(int(x) for x in tables.reshape(-1)[::3]))
+        sel = torch.as_tensor(blocks, device=wl.k_pool.device)
+        wl.k_pool[:, sel, :, 0:6, :] *= case.small_keys
     glob = wl.global_scores
     if n_cap != wl.n_cap:
         g2 = torch.rand((glob.shape[0], glob.shape[1], glob.shape[2], n_cap),
@@ -172,7 +190,7 @@ def run_case(case: Case, device: str = "cuda") -> Result:
     spec = case.spec
     res = Result(ok=True)
     wl, glob, host, dev, tables, dst, pinned, n_tok, bm_plan = build_inputs(case, device)
-    zparams, oparams = _params_for(spec, case.flags)
+    zparams, oparams = _params_for(spec, case.flags, case.weights, case.sm_scale)
     pool = Z.make_pool(wl.k_pool, wl.v_pool)
     R, L, H = spec.requests, spec.layers, spec.kv_heads
     U = R * L * H

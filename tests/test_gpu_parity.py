@@ -15,6 +15,7 @@ import torch
 import oracle as O
 import kv_cache_compression_paged_amd as Z
 from kv_cache_compression_paged_amd import synth
+from tests import fullsize as F
 from tests import parity as P
 
 pytestmark = pytest.mark.gpu
@@ -250,6 +251,27 @@ def test_duplicate_slots_are_rejected(flags):
                 assert np.all(np.abs(g_now[r, l, h] - gref) <= 1e-4 * np.abs(gref) + 1e-6)
 
 
+SCHEDULES = pytest.mark.parametrize("flags", [0, Z.ZP_SPLIT_UNITS],
+                                    ids=["one-workgroup", "split-units"])
+
+
+@SCHEDULES
+def test_non_default_weights_and_softmax_scale(flags):
+    # s = 0.7 attn + 1.3 global - 0.2 red with an explicit scale 0.05: the
+    # weights enter the kernels' fused score and the scale their exp2 domain
+    _check(P.Case(EIGHT_B, flags=flags, weights=(0.7, 1.3, 0.2), sm_scale=0.05),
+           "weights 0.7/1.3/0.2, sm_scale 0.05")
+
+
+@SCHEDULES
+@pytest.mark.parametrize("scale", [0.0, 1e-6], ids=["zero-norm", "tiny-norm"])
+def test_small_norm_keys_hit_the_cosine_clamp(flags, scale):
+    # zero keys (cosine 0 with every key) and keys of norm ~1e-5, whose
+    # pairwise norm products fall below the 1e-8 clamp
+    _check(P.Case(EIGHT_B, flags=flags, small_keys=scale,
+                  weights=(1.0, 0.5, 2.0)), f"keys scaled by {scale}")
+
+
 def _forced_global(spec, evict_positions):
     g = np.zeros((spec.requests, spec.layers, spec.kv_heads, spec.n_tokens))
     g[..., list(evict_positions)] = -100.0
@@ -367,26 +389,40 @@ def _check_sampled_units(spec, wl, out, saved, pinned, dst_dev, unit_base=0,
         assert np.all(np.abs(gn - gref) <= 1e-4 * np.abs(gref) + 1e-6)
 
 
-def _sample_units(U, n_samples, seed):
+def _sample_units(R, L, H, n_samples, seed):
+    """A seeded sample spread over requests, layers and heads (unit 0 and the
+    last unit always included)."""
     rng = np.random.default_rng(seed)
-    units = set(int(x) for x in rng.choice(U, size=n_samples, replace=False))
-    return sorted(units | {0, U - 1})
+    U = R * L * H
+    units = {0, U - 1}
+    i = 0
+    while len(units) < min(U, n_samples + 2):
+        r = int(rng.integers(R))
+        l, h = i % L, (i + i // L) % H
+        units.add((r * L + l) * H + h)
+        i += 1
+    return sorted(units)
 
 
-def _full_size_sampled(spec, n_samples, seed, fused=False, flags=0):
-    """Run the full call and check sampled units against the oracle. With
-    fused=True the global update runs inside the compression kernel
-    (ZP_UPDATE_GLOBAL), the launch configuration bench.py times; `flags` adds
-    schedule bits (ZP_SPLIT_UNITS)."""
+def _full_size(spec, n_samples, seed, fused=False, flags=0):
+    """Run the full call and check it. Every unit: keep = top k of its own
+    scores, compacted K/V rows = the original rows through keep (against an
+    untouched copy of the pool, or, with target blocks, against the sources,
+    which are checked to be unchanged), global rows = g[keep] + attn[keep]
+    bit for bit. A seeded sample of units: everything against the oracle.
+    With fused=True the global update runs inside the compression kernel
+    (ZP_UPDATE_GLOBAL), the launch configuration bench.py times; `flags`
+    adds schedule bits (ZP_SPLIT_UNITS)."""
     dev = "cuda"
     _say(f"[full] generating {spec.name}")
     wl = synth.make(spec, device=dev)
     R, L, H, b = spec.requests, spec.layers, spec.kv_heads, spec.block_size
     U = R * L * H
-    k = spec.keep
-    units = _sample_units(U, n_samples, seed)
+    k, n = spec.keep, spec.n_tokens
+    units = _sample_units(R, L, H, n_samples, seed)
     tables = wl.tables
-    if spec.shared_blocks:
+    shared = bool(spec.shared_blocks)
+    if shared:
         bm = Z.BlockManager(spec.pool_blocks)
         bm.alloc(spec.pool_blocks)
         for bid in range(spec.pool_blocks):
@@ -401,6 +437,16 @@ def _full_size_sampled(spec, n_samples, seed, fused=False, flags=0):
         dst, pinned = tables.copy(), np.zeros(R, dtype=np.int32)
     tab_dev = torch.from_numpy(tables).to(dev)
     saved = _save_units(spec, wl, tab_dev, units)
+    g0 = wl.global_scores.clone()
+    hasher = F.RowHasher(spec.head_dim, dev)
+    if shared:
+        # the sources are never written with target blocks: their hashes now
+        # and after the call show it, and they then serve as the original rows
+        src_h = [F.hash_logical_rows(hasher, p_, tab_dev, spec.n_max)
+                 for p_ in (wl.k_pool, wl.v_pool)]
+        k0, v0 = wl.k_pool, wl.v_pool
+    else:
+        k0, v0 = wl.k_pool.clone(), wl.v_pool.clone()
     zparams, _ = P._params_for(spec, flags | (Z.ZP_UPDATE_GLOBAL if fused else 0))
     pool = Z.make_pool(wl.k_pool, wl.v_pool)
     batch = Z.DeviceBatch(
@@ -418,41 +464,58 @@ def _full_size_sampled(spec, n_samples, seed, fused=False, flags=0):
         Z.zp_update_global(wl.global_scores, pool, batch, out, zparams)
     torch.cuda.synchronize()
     assert Z.zp_workspace_error(ws) == Z.ZP_OK
-    _check_all_units(spec, out, wl.global_scores, bool(spec.shared_blocks))
+    _check_all_units(spec, out, wl.global_scores, shared)
+    F.check_keep_is_topk_of_own_scores(out.keep_idx, out.score, n)
+    F.check_global_rows(wl.global_scores, g0, out.keep_idx, out.attn, wl.slots, L, H)
+    if shared:
+        for p_, h0, what in ((wl.k_pool, src_h[0], "K"), (wl.v_pool, src_h[1], "V")):
+            assert torch.equal(F.hash_logical_rows(hasher, p_, tab_dev, spec.n_max), h0), \
+                f"{what} source rows changed"
+        del src_h
+    F.check_rows_against_copy(wl.k_pool, k0, tab_dev, batch.dst_table, out.keep_idx,
+                              n, spec.n_max, in_place=not shared, what="K")
+    F.check_rows_against_copy(wl.v_pool, v0, tab_dev, batch.dst_table, out.keep_idx,
+                              n, spec.n_max, in_place=not shared, what="V")
+    _say(f"[full] {spec.name}: all {U} units: keep = top-k of own scores, "
+         "rows and global rows exact")
+    del k0, v0, g0
     _check_sampled_units(spec, wl, out, saved, pinned, batch.dst_table)
-    _say(f"[full] {spec.name}: {len(units)} sampled units match")
+    _say(f"[full] {spec.name}: {len(units)} sampled units match the oracle")
     del wl, out
     torch.cuda.empty_cache()
 
 
-def test_full_size_small_model_sampled():
-    _full_size_sampled(synth.SMALL, 6, 11)
+def test_full_size_small_model():
+    _full_size(synth.SMALL, 64, 11)
 
 
-def test_full_size_8b_sampled():
+def test_full_size_8b():
     # the timed launch: global update inside the compression kernel
-    _full_size_sampled(synth.EIGHT_B, 6, 12, fused=True)
+    _full_size(synth.EIGHT_B, 64, 12, fused=True)
 
 
-def test_full_size_8b_split_sampled():
+def test_full_size_8b_split():
     # the same batch on the split-unit schedule (bench.py --split-units)
-    _full_size_sampled(synth.EIGHT_B, 6, 14, fused=True, flags=Z.ZP_SPLIT_UNITS)
+    _full_size(synth.EIGHT_B, 64, 14, fused=True, flags=Z.ZP_SPLIT_UNITS)
 
 
-def test_full_size_prefix_sampled():
+def test_full_size_prefix():
     # 256 requests in 4 groups sharing 32 leading blocks each: the pinned
     # prefix stays in place and the kept private rows go to fresh targets
-    _full_size_sampled(synth.PREFIX, 6, 13)
+    _full_size(synth.PREFIX, 64, 13)
 
 
-def test_full_size_overlap_sampled():
+def test_full_size_overlap():
     """512 requests in 8 groups. Step 0: group 0 (64 requests, all 32 layers,
     holding the query slots) is compressed on one stream while the other 448
     requests decode on a second stream. Step 1: group 1 compresses while group
-    0, now compacted to k tokens, decodes with the rest. Sampled compressed
-    units, sampled decode pairs of step 0, and sampled decode pairs of the
-    compacted group (against the oracle's attention over the kept tokens of
-    the original cache) are checked."""
+    0, now compacted to k tokens, decodes with the rest. Checked: every
+    compressed unit of both steps (keep = top k of its own scores, global rows
+    bit-exact; the compacted rows of step 0 against hashes of the original
+    rows, since a 256 GiB pool leaves no room for a copy), 64 sampled
+    compressed units against the oracle, sampled decode pairs of step 0, and
+    sampled decode pairs of the compacted group (against the oracle's
+    attention over the kept tokens of the original cache)."""
     spec = synth.OVERLAP
     dev = "cuda"
     per = spec.requests // spec.compress_groups
@@ -466,8 +529,12 @@ def test_full_size_overlap_sampled():
     tab_c = torch.from_numpy(np.ascontiguousarray(tables[grp])).to(dev)
     tab_d = torch.from_numpy(np.ascontiguousarray(tables[rest])).to(dev)
     Uc = per * L * H
-    units = _sample_units(Uc, 6, 14)
+    units = _sample_units(per, L, H, 64, 14)
     saved = _save_units(spec, wl, tab_c, units)
+    hasher = F.RowHasher(spec.head_dim, dev)
+    row_h = [F.hash_logical_rows(hasher, p_, tab_c, spec.n_max)
+             for p_ in (wl.k_pool, wl.v_pool)]
+    g0 = wl.global_scores.clone()
     rng = np.random.default_rng(spec.seed + 3)
     lens = rng.integers(k + 1, n, size=rest.size).astype(np.int32)  # U{k+1..N-1}
     q = synth.decode_queries(spec, rest.size, dev, spec.seed + 4)
@@ -506,6 +573,14 @@ def test_full_size_overlap_sampled():
     torch.cuda.synchronize()
     assert Z.zp_workspace_error(ws) == Z.ZP_OK
     _check_all_units(spec, out, wl.global_scores, False)
+    F.check_keep_is_topk_of_own_scores(out.keep_idx, out.score, n)
+    F.check_global_rows(wl.global_scores, g0, out.keep_idx, out.attn, range(per), L, H)
+    for p_, h0, what in ((wl.k_pool, row_h[0], "K"), (wl.v_pool, row_h[1], "V")):
+        F.check_rows_against_hashes(hasher, p_, h0, batch.dst_table, out.keep_idx,
+                                    spec.n_max, in_place=True, what=what)
+    del row_h
+    _say(f"[full] {spec.name}: all {Uc} compressed units: keep = top-k of own "
+         "scores, row hashes and global rows exact")
     _check_sampled_units(spec, wl, out, saved, np.zeros(per, dtype=np.int32),
                          batch.dst_table)
     _say(f"[full] {spec.name}: {len(units)} sampled compressed units match")
@@ -545,6 +620,7 @@ def test_full_size_overlap_sampled():
     dec1 = torch.full((dec_reqs.size, L, spec.q_heads, spec.head_dim), float("nan"),
                       dtype=torch.float32, device=dev)
     lens1_dev = torch.from_numpy(lens1).to(dev)
+    g0.copy_(wl.global_scores)
     ready.record(torch.cuda.current_stream())
     sc.wait_event(ready)
     sd.wait_event(ready)
@@ -556,6 +632,8 @@ def test_full_size_overlap_sampled():
     torch.cuda.synchronize()
     assert Z.zp_workspace_error(ws) == Z.ZP_OK
     _check_all_units(spec, out, wl.global_scores, False)
+    F.check_keep_is_topk_of_own_scores(out.keep_idx, out.score, n)
+    F.check_global_rows(wl.global_scores, g0, out.keep_idx, out.attn, range(per), L, H)
     q1h = synth.raw_numpy(q1)
     got1 = dec1.cpu().numpy().astype(np.float64)
     for (r, l) in pairs0:  # group 0 comes first in dec_reqs
