@@ -21,7 +21,12 @@ below):
   S2 a request needs its last w queries captured before it compresses, so a
      slot-free request stops decoding once its cache reaches N_max*b - w
      tokens and waits for a slot; slot holders capture every decoded token,
-     and an admitted slot holder has its prompt's last min(w, len) queries;
+     and an admitted slot holder has its prompt's last min(w, len) queries.
+     This is stricter than the pages, which let a slot-free request decode
+     until it holds N_max blocks and its last block is full ([de] §2,
+     [zh] §2.2): it stops w tokens earlier (for w > b, whole blocks
+     earlier), because a request that got its slot only at the trigger
+     would hold no captured window to score with;
   S3 a slot holder compresses in the step after its cache reaches N_max*b
      tokens (or at admission, for a longer prompt), provided it has w
      captured queries; it does not decode in that step;
@@ -101,6 +106,14 @@ class Scheduler:
         self.waiting.append(rid)
 
     # ------------------------------------------------------------ helpers
+    def _slot_holders(self) -> List[int]:
+        """S1: the first M running requests, in admission order."""
+        return self.running[:self.M]
+
+    def _slot_free_stop(self) -> int:
+        """S2: a request without a slot decodes only below this many tokens."""
+        return self.n_max * self.b - self.w
+
     def _release(self, table: List[int]) -> None:
         for bid in table:
             self.pool.refcount[bid] -= 1
@@ -133,7 +146,7 @@ class Scheduler:
         trig = nmax * b
         plan = StepPlan(False, [], [], [], [], [])
         # S1: slots for the first M running requests
-        for rid in self.running[:self.M]:
+        for rid in self._slot_holders():
             r = self.reqs[rid]
             if r.slot < 0:
                 r.slot, r.captured = self._take_slot(), 0
@@ -172,7 +185,7 @@ class Scheduler:
             if rid in skip:
                 continue
             r = self.reqs[rid]
-            if r.slot < 0 and r.n >= trig - w:
+            if r.slot < 0 and r.n >= self._slot_free_stop():
                 continue
             if r.slot >= 0 and r.n >= trig:
                 continue
@@ -205,7 +218,7 @@ class Scheduler:
             shared = len(self.prefixes[q.group]) if q.group >= 0 else 0
             need = (length + b - 1) // b - shared
             gets_slot = len(self.running) < self.M
-            if length >= trig - w and not gets_slot:
+            if length >= self._slot_free_stop() and not gets_slot:
                 break
             if need > len(self.pool.stack):
                 break
