@@ -299,6 +299,27 @@ zp_status zp_paged_decode_split(float* out, const void* q, const void* k_new,
                                 const zp_params* params, int32_t splits, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * split-K decode as zp_paged_decode_split, with its split partials in a
+ * static device array of ZP_DECODE_STATIC_BYTES owned by the library (each
+ * GPU the library runs on holds one copy until the process ends) instead of
+ * a caller workspace. The call allocates nothing and issues no memset; the
+ * caller still passes every input and output. Calls that overlap on one GPU
+ * (on different streams, or from several threads) share that array and
+ * race: serialise them. The array keeps the last call's partials; nothing
+ * in it needs clearing between calls. Call with the stream's device current.
+ * Errors: as zp_paged_decode_split, with ZP_EWORKSPACE when the partials,
+ * num_reqs * layers * q_heads * splits * (head_dim + 2) * 4 bytes, exceed
+ * ZP_DECODE_STATIC_BYTES (nothing is enqueued then). */
+#define ZP_DECODE_STATIC_BYTES (64u << 20)
+zp_status zp_paged_decode_split_static(float* out, const void* q, const void* k_new,
+                                       const void* v_new, const zp_kv_pool* pool,
+                                       const int32_t* block_tables, int32_t max_blocks,
+                                       const int32_t* seq_lens, int32_t num_reqs,
+                                       const zp_params* params, int32_t splits,
+                                       void* stream);
+
 /* All-pairs key redundancy, an ablation of the lightning score ([zh] §2.1,
  * [fr] §2.E: the original score compared every pair of cached keys, O(N^2 b^2)
  * for N blocks of b; lightning keeps the pairs inside a block, O(N b^2)).

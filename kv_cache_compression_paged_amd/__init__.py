@@ -46,13 +46,16 @@ ZP_KERNEL_DECODE = 2
 ZP_KERNEL_CAPTURE = 3
 ZP_KERNEL_REDUNDANCY_FULL = 4
 ZP_KERNEL_KINDS = 5
+
+ZP_DECODE_STATIC_BYTES = 64 << 20
 KERNEL_NAMES = ("compress", "global_update", "paged_decode", "capture",
                 "redundancy_full")
 
 EXPORTED = (
     "zp_compress_workspace_bytes", "zp_compress", "zp_update_global",
     "zp_workspace_error", "zp_paged_decode", "zp_paged_decode_append",
-    "zp_decode_workspace_bytes", "zp_paged_decode_split", "zp_capture_queries",
+    "zp_decode_workspace_bytes", "zp_paged_decode_split", "zp_paged_decode_split_static",
+    "zp_capture_queries",
     "zp_redundancy_full",
     "zp_sched_create", "zp_sched_destroy", "zp_sched_block_manager",
     "zp_sched_add_prefix", "zp_sched_submit", "zp_sched_step", "zp_sched_complete",
@@ -141,6 +144,7 @@ def lib() -> ctypes.CDLL:
         "zp_paged_decode_append": (I32, [P, P, P, P, P, P, I32, P, I32, P, P]),
         "zp_decode_workspace_bytes": (I32, [P, P, I32, I32, P]),
         "zp_paged_decode_split": (I32, [P, P, P, P, P, P, I32, P, I32, P, I32, P, U, P]),
+        "zp_paged_decode_split_static": (I32, [P, P, P, P, P, P, I32, P, I32, P, I32, P]),
         "zp_bm_create": (P, [I32]),
         "zp_bm_destroy": (None, [P]),
         "zp_bm_alloc": (I32, [P, I32, P]),
@@ -345,6 +349,19 @@ def zp_paged_decode_split(out, q, pool: KVPool, block_tables, seq_lens,
                                        _ptr(seq_lens), R, ctypes.byref(params), splits,
                                        _ptr(workspace), nbytes, _stream_handle(stream)),
            "zp_paged_decode_split")
+
+
+def zp_paged_decode_split_static(out, q, pool: KVPool, block_tables, seq_lens,
+                                 params: Params, splits: int, k_new=None, v_new=None,
+                                 stream=None) -> None:
+    """Split-K decode with the partials in the library's static device
+    scratch (no workspace argument; see include/zipage.h)."""
+    R, mb = block_tables.shape
+    _check(lib().zp_paged_decode_split_static(_ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                              ctypes.byref(pool), _ptr(block_tables), mb,
+                                              _ptr(seq_lens), R, ctypes.byref(params),
+                                              splits, _stream_handle(stream)),
+           "zp_paged_decode_split_static")
 
 
 def zp_redundancy_full(red_block, pool: KVPool, batch: DeviceBatch, params: Params,
@@ -605,7 +622,8 @@ __all__: Tuple[str, ...] = (
     "alloc_workspace", "zp_compress_workspace_bytes", "zp_compress",
     "zp_update_global", "zp_workspace_error", "zp_paged_decode",
     "zp_capture_queries", "zp_paged_decode_append", "zp_decode_workspace_bytes",
-    "zp_paged_decode_split", "zp_redundancy_full", "Scheduler", "SchedPlan",
+    "zp_paged_decode_split", "zp_paged_decode_split_static", "zp_redundancy_full",
+    "Scheduler", "SchedPlan",
     "timing_enable", "timing_read", "BlockManager", "Plan", "version",
     "EXPORTED",
 )

@@ -260,9 +260,15 @@ zp_status zp_workspace_error(void* workspace, void* stream, int32_t* code) {
   return ZP_OK;
 }
 
+}  // extern "C"
+
 namespace {
 
 constexpr int kMaxSplits = 256;
+
+}  // namespace
+
+namespace zp {
 
 size_t decode_ws_bytes(const zp_kv_pool* pool, const zp_params* params, int32_t num_reqs,
                        int32_t splits) {
@@ -270,7 +276,7 @@ size_t decode_ws_bytes(const zp_kv_pool* pool, const zp_params* params, int32_t 
          (pool->head_dim + 2) * sizeof(float);
 }
 
-// Shared checks and launch of the three decode entry points.
+// Shared checks and launch of the decode entry points.
 zp_status decode_common(const char* name, float* out, const void* q, const void* k_new,
                         const void* v_new, const zp_kv_pool* pool,
                         const int32_t* block_tables, int32_t max_blocks,
@@ -337,7 +343,9 @@ zp_status decode_common(const char* name, float* out, const void* q, const void*
   return st;
 }
 
-}  // namespace
+}  // namespace zp
+
+extern "C" {
 
 zp_status zp_paged_decode(float* out, const void* q, const zp_kv_pool* pool,
                           const int32_t* block_tables, int32_t max_blocks,

@@ -10,6 +10,8 @@
 // the keys, so V rows are read as coalesced 256-byte segments.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "zp_device.h"
 #include "zp_host.h"
 
@@ -329,3 +331,69 @@ zp_status launch_decode(const DecodeGeom& g, const DecodeIO& io, const zp_kv_poo
 }
 
 }  // namespace zp
+
+// ---------------------------------------------------------------------------
+// Split-K decode for callers that cannot allocate device memory (code under
+// HIP graph capture, tight serving loops): the split partials live in
+// `scratch`, a file-scope device array of ZP_DECODE_STATIC_BYTES that every
+// GPU the library runs on holds until the process ends. In host code the
+// array's name is only a stand-in symbol, never a device address: the
+// address of each GPU's copy comes from hipGetSymbolAddress, taken once per
+// device (with that device current) and kept, and only that address is
+// passed to the kernels. Nothing in the scratch has to start at zero: every
+// split of every unit the merge kernel reads has written its partials
+// earlier on the same stream. Calls that overlap on one GPU share the array
+// and race.
+static __device__ __align__(256) char scratch[ZP_DECODE_STATIC_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+zp_status scratch_on_current_device(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess)
+    return zp::fail(ZP_EHIP, "zp_paged_decode_split_static: hipGetDevice: %s",
+                    hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return zp::fail(ZP_EUNSUPPORTED, "zp_paged_decode_split_static: device %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return zp::fail(ZP_EHIP, "zp_paged_decode_split_static: scratch address: %s",
+                      hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return ZP_OK;
+}
+
+}  // namespace
+
+extern "C" zp_status zp_paged_decode_split_static(
+    float* out, const void* q, const void* k_new, const void* v_new, const zp_kv_pool* pool,
+    const int32_t* block_tables, int32_t max_blocks, const int32_t* seq_lens,
+    int32_t num_reqs, const zp_params* params, int32_t splits, void* stream) {
+  if (!pool || !params || num_reqs < 0 || splits < 1 || params->q_heads <= 0 ||
+      pool->layers < 1 || pool->head_dim < 1)
+    return zp::fail(ZP_EINVAL, "zp_paged_decode_split_static: bad arguments");
+  const size_t need = splits > 1 ? zp::decode_ws_bytes(pool, params, num_reqs, splits) : 0;
+  if (need > static_cast<size_t>(ZP_DECODE_STATIC_BYTES))
+    return zp::fail(ZP_EWORKSPACE, "zp_paged_decode_split_static: %zu bytes of split "
+                    "partials exceed the %zu-byte static scratch (use fewer requests "
+                    "or splits, or zp_paged_decode_split with a workspace)", need,
+                    static_cast<size_t>(ZP_DECODE_STATIC_BYTES));
+  void* ws = nullptr;
+  if (splits > 1) {
+    const zp_status st = scratch_on_current_device(&ws);
+    if (st != ZP_OK) return st;
+  }
+  return zp::decode_common("zp_paged_decode_split_static", out, q, k_new, v_new, pool,
+                           block_tables, max_blocks, seq_lens, num_reqs, params, splits, ws,
+                           static_cast<size_t>(ZP_DECODE_STATIC_BYTES), stream);
+}

@@ -66,6 +66,16 @@ struct DecodeIO {
 };
 zp_status launch_decode(const DecodeGeom& g, const DecodeIO& io, const zp_kv_pool& pool,
                         void* stream);
+// Bytes of split partials a decode call needs, and the checks + launch that
+// every decode entry point shares (api.cpp).
+size_t decode_ws_bytes(const zp_kv_pool* pool, const zp_params* params, int32_t num_reqs,
+                       int32_t splits);
+zp_status decode_common(const char* name, float* out, const void* q, const void* k_new,
+                        const void* v_new, const zp_kv_pool* pool,
+                        const int32_t* block_tables, int32_t max_blocks,
+                        const int32_t* seq_lens, int32_t num_reqs,
+                        const zp_params* params, int32_t splits, void* workspace,
+                        size_t workspace_bytes, void* stream);
 
 // Timing hooks: record an event pair around kernel `kind` when enabled.
 void timing_before(int kind, void* stream);

@@ -352,6 +352,21 @@ def test_decode_append_and_split_reject_bad_arguments():
     assert split(4, R=0) == Z.ZP_OK
 
 
+def test_static_split_decode_refuses_oversized_partials_before_any_gpu_call():
+    """The allocation-free split-K decode checks its partials against the
+    library's static array first: beyond it the call fails with
+    ZP_EWORKSPACE and touches nothing (so it runs without a GPU here)."""
+    pool = Z.KVPool(FAKE, FAKE, 16, 32, 8, 16, 128, Z.ZP_BF16)
+    params = Z.make_params(8, 32, 32, Z.ZP_BF16)
+    lib = Z.lib()
+    # 128 requests x 32 layers x 32 heads x 64 splits x 130 x 4 B > 64 MiB
+    st = lib.zp_paged_decode_split_static(FAKE, FAKE, None, None, ctypes.byref(pool),
+                                          FAKE, 8, FAKE, 128, ctypes.byref(params),
+                                          64, None)
+    assert st == Z.ZP_EWORKSPACE
+    assert "static scratch" in Z.last_error()
+
+
 def test_decode_workspace_formula():
     pool, prm = _pool(), _params()
     # R * layers * q_heads * splits * (head_dim + 2) floats; none for one split
