@@ -65,6 +65,8 @@ def parse():
                     help="run the global-score update as its own launch")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 1 GiB device copy first (counter scaling)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time the 8B-like workload alone (skip the other workloads)")
     ap.add_argument("--split-units", action="store_true",
                     help="time the split-unit schedule (ZP_SPLIT_UNITS) instead of one "
                          "workgroup per unit")
@@ -74,15 +76,17 @@ def parse():
 def unit_bytes(spec, M: np.ndarray) -> dict:
     """Algorithmic bytes per unit, summed over units, for one step.
 
-    whole step: s*d*(N + 4M) + s_q*w*G*d + 12*N_cap (keys read once, moved K
-    and V rows read and written, the window, global read for scoring plus the
-    read and write of the update); per kernel:
-      compress: s*d*N + s_q*w*G*d + 4N (global) + 4N (attn out) + 4k (keep)
-                + 4*M*d*s (moved K and V rows, read and written)
-      global:   8*N_cap + 8k (row read/write, keep and attn at kept)
+    whole step: B_alg = s*d*(N + 4M) + s_q*w*G*d + 12*N_cap -- keys read once,
+    the M moved K and V rows read and written, the window, the global row read
+    for scoring plus read and written by the update. The kernels split it:
+      compress:      s*d*(N + 4M) + s_q*w*G*d + 4*N_cap (global read)
+      global_update: 8*N_cap (row read and written)
+    so with the update inside the compression kernel (ZP_UPDATE_GLOBAL) the
+    kernel's bytes are the step's B_alg. Outputs the method does not need in
+    HBM to be consumed later (attention row, keep row) are not counted.
     """
     s = 2 if spec.dtype == "bf16" else 4
-    d, N, k = spec.head_dim, spec.n_tokens, spec.keep
+    d, N = spec.head_dim, spec.n_tokens
     G = spec.q_heads // spec.kv_heads
     wGd = spec.window * G * d * s
     U = M.size
@@ -90,8 +94,8 @@ def unit_bytes(spec, M: np.ndarray) -> dict:
     Msum = float(M.sum())
     return {
         "step": U * (s * d * N + wGd + 12 * n_cap) + 4.0 * s * d * Msum,
-        "compress": U * (s * d * N + wGd + 4 * N + 4 * N + 4 * k) + 4.0 * s * d * Msum,
-        "global_update": U * (8 * n_cap + 8 * k),
+        "compress": U * (s * d * N + wGd + 4 * n_cap) + 4.0 * s * d * Msum,
+        "global_update": U * (8 * n_cap),
     }
 
 
@@ -182,12 +186,14 @@ def cpu_baseline(spec, wl, seconds: float) -> dict:
     tokens_per_s = done * n / (L * H) / t_cpu
     return {"value": tokens_per_s, "unit": "tokens/s", "cores": blas_threads,
             "kind": "oracle", "cpu": _cpu_model(), "host_cpus": os.cpu_count(),
-            "blas": blas_name,
-            "sample": f"{done} seeded (request, layer, kv_head) units of this "
-                      f"workload, full oracle chain (score, select, K/V "
-                      f"compaction, global update), {t_cpu:.1f} s; numpy's "
-                      f"BLAS on up to {blas_threads} threads, the rest of the "
-                      f"oracle on one; a token covers {L * H} units"}
+            "blas": blas_name, "extrapolated": done < R * L * H,
+            "units_timed": done, "units_in_workload": R * L * H,
+            "sample": f"extrapolated linearly from {done} of {R * L * H} seeded "
+                      f"(request, layer, kv_head) units of this workload: full "
+                      f"oracle chain (score, select, K/V compaction, global "
+                      f"update) in {t_cpu:.1f} s; numpy's BLAS on up to "
+                      f"{blas_threads} threads, the rest of the oracle on one; "
+                      f"a token covers {L * H} units"}
 
 
 def decode_bytes(spec, lens: np.ndarray) -> float:
@@ -200,7 +206,7 @@ def decode_bytes(spec, lens: np.ndarray) -> float:
             + R * L * Hq * d * (s + 4))
 
 
-def run_overlap(args, spec):
+def run_overlap(args, spec, steps: int, warm: int) -> dict:
     """Compression of one group overlapped with decoding of the others."""
     import torch
     import kv_cache_compression_paged_amd as Z
@@ -232,7 +238,6 @@ def run_overlap(args, spec):
     gen.manual_seed(spec.seed + 500)
     rng = np.random.default_rng(spec.seed + 501)
     sc, sd = torch.cuda.Stream(), torch.cuda.Stream()
-    steps, warm = args.steps, args.warmup
     compressed = set()
     rec = {"C": [], "D": [], "CD": [], "bytes_C": [], "bytes_D": []}
 
@@ -335,7 +340,10 @@ def run_overlap(args, spec):
                      "traffic": None,
                      "alg_bytes_per_launch": round(b_c + b_d)},
     }
-    print(json.dumps(result), flush=True)
+    del wl, out, ws, q, dec
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return result
 
 
 def run_capture(args):
@@ -528,6 +536,85 @@ def run_redundancy_ablation(args):
     }), flush=True)
 
 
+def run_redundancy_sweep(args):
+    """Time against N_max of the all-pairs redundancy and of the whole
+    lightning compression step (score, select, compaction; the lightning
+    score is fused into its key sweep) on the same units: 4 requests x 32
+    layers x 8 KV heads (1024 units) of the 8B-like layout, b = 16, N_max in
+    {64, ..., 1024}. Fits t ~ N_max^p by least squares in log-log space: the
+    pages' claim is O(N^2 b^2) for the all-pairs score against O(N b^2) for
+    the lightning one ([zh] §2.1)."""
+    import torch
+    import kv_cache_compression_paged_amd as Z
+    from kv_cache_compression_paged_amd import synth
+    dev = "cuda"
+    reps = max(args.steps, 1)
+    rows = []
+    for n_max in (64, 128, 256, 512, 1024):
+        spec = synth.scaled(synth.EIGHT_B, requests=4, n_max=n_max, pool_blocks=4 * n_max)
+        wl = synth.make(spec, device=dev)
+        R, L, H, d, n = spec.requests, spec.layers, spec.kv_heads, spec.head_dim, spec.n_tokens
+        U = R * L * H
+        params = Z.make_params(spec.n_max, spec.window, spec.q_heads, Z.ZP_BF16)
+        pool = Z.make_pool(wl.k_pool, wl.v_pool)
+        tab = torch.from_numpy(wl.tables).to(dev)
+        batch = Z.DeviceBatch(slot=torch.arange(R, dtype=torch.int32, device=dev),
+                              n_tokens=torch.full((R,), n, dtype=torch.int32, device=dev),
+                              src_table=tab, dst_table=tab.clone(),
+                              n_pinned=torch.zeros(R, dtype=torch.int32, device=dev),
+                              num_slots=R, n_cap=n)
+        ws = Z.alloc_workspace(pool, params, R, dev)
+        red_b = torch.empty((U, n), device=dev)
+        red_a = torch.empty((U, n), device=dev)
+        out = Z.alloc_outputs(U, spec.keep, n, dev)
+
+        def timed(fn, kind):
+            fn()
+            torch.cuda.synchronize()
+            Z.timing_read()
+            Z.timing_enable(True)
+            for _ in range(reps):
+                fn()
+            torch.cuda.synchronize()
+            Z.timing_enable(False)
+            cnt, tot = Z.timing_read()[kind]
+            return tot / cnt
+
+        t_all = timed(lambda: Z.zp_redundancy_full(red_b, pool, batch, params, ws,
+                                                   red_all=red_a), "redundancy_full")
+        t_comp = timed(lambda: Z.zp_compress(pool, batch, wl.q_window, wl.global_scores,
+                                             params, out, ws), "compress")
+        if Z.zp_workspace_error(ws) != Z.ZP_OK:
+            raise RuntimeError("device error in the sweep")
+        flops = U * 2.0 * n * n * d
+        rows.append({"n_max": n_max, "tokens": n, "all_pairs_ms": round(t_all, 4),
+                     "compress_ms": round(t_comp, 4),
+                     "all_pairs_TFLOPs": round(flops / (t_all * 1e-3) / 1e12, 1),
+                     "ratio": round(t_all / t_comp, 2)})
+        print(f"[bench] sweep N_max {n_max}: all-pairs {t_all:.3f} ms, compress "
+              f"{t_comp:.3f} ms", file=sys.stderr, flush=True)
+        del wl, out, red_b, red_a, batch, pool
+        torch.cuda.empty_cache()
+    x = np.log([r["n_max"] for r in rows])
+    p_all = float(np.polyfit(x, np.log([r["all_pairs_ms"] for r in rows]), 1)[0])
+    p_comp = float(np.polyfit(x, np.log([r["compress_ms"] for r in rows]), 1)[0])
+    best = max(r["all_pairs_TFLOPs"] for r in rows)
+    print(json.dumps({
+        "metric": "time against N_max: all-pairs redundancy vs the lightning compression step",
+        "value": round(p_all, 3), "unit": "fitted exponent of the all-pairs time",
+        "n_gpus": 1, "steps": reps, "warmup": 1, "ms_per_step": rows[-1]["all_pairs_ms"],
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "redundancy_sweep_1024units", "units": 1024,
+                   "block_size": 16, "head_dim": 128, "n_max": [r["n_max"] for r in rows]},
+        "exponent_all_pairs": round(p_all, 3), "exponent_compress": round(p_comp, 3),
+        "rows": rows,
+        "roofline": {"bound": "mfma", "kernel": "redundancy_full", "achieved": best,
+                     "peak": 2500.0, "unit": "TFLOP/s", "frac": round(best / 2500.0, 4),
+                     "traffic": None, "alg_bytes_per_launch": None},
+    }), flush=True)
+
+
 def run_engine(args):
     """The engine loop at the 8B-like layout (32 layers, 8 KV heads, 32 query
     heads of 128, b = 16, N_max = 256, w = 32): 96 running requests, each
@@ -584,36 +671,13 @@ def run_engine(args):
     }), flush=True)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the "
-              "compression path needs no collective, see the design notes on "
-              "sharding.", file=sys.stderr)
-        sys.exit(2)
+def measure_compress(spec, args, steps: int, warm: int, with_cpu: bool,
+                     with_copy: bool = True) -> dict:
+    """Times `steps` compression steps of one workload and returns its JSON
+    record (the device memory of the workload is released on return)."""
     import torch
     import kv_cache_compression_paged_amd as Z
     from kv_cache_compression_paged_amd import synth
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    Z.lib()
-    if args.workload == "capture_8b_32L_32q":
-        run_capture(args)
-        return
-    if args.workload == "decode_8b_32L_8kv_32q":
-        run_decode(args)
-        return
-    if args.workload == "redundancy_ablation_8b":
-        run_redundancy_ablation(args)
-        return
-    if args.workload == "engine_8b":
-        run_engine(args)
-        return
-    spec = synth.SPECS[args.workload]
-    if spec.compress_groups > 1:
-        run_overlap(args, spec)
-        return
     dev = "cuda"
     print(f"[bench] generating {spec.name}", file=sys.stderr, flush=True)
     t_gen = time.perf_counter()
@@ -659,7 +723,6 @@ def main():
         num_slots=R, n_cap=wl.n_cap)
     out = Z.alloc_outputs(U, k, wl.n_cap, dev)
     ws = Z.alloc_workspace(pool, params, R, dev)
-    steps, warm = args.steps, args.warmup
     holes = torch.empty((warm + steps, U), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
     # Every step gets its own global-score rows drawn U[0,1) like the
@@ -672,18 +735,21 @@ def main():
     for _ in range(warm + steps - 1):
         globs.append(torch.rand(wl.global_scores.shape, generator=gen,
                                 device=dev, dtype=torch.float32))
-    # the device's own copy rate: a plain 2 GiB device-to-device copy
-    csrc = torch.empty(1 << 29, dtype=torch.float32, device=dev).fill_(1.0)
-    cdst = torch.empty_like(csrc)
-    cdst.copy_(csrc)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(5):
+    copy_gbps = None
+    if with_copy:
+        # the device's copy rate as torch's own device-to-device copy gives
+        # it (2 GiB); this is not a peak: the step's traffic mix runs faster
+        csrc = torch.empty(1 << 29, dtype=torch.float32, device=dev).fill_(1.0)
+        cdst = torch.empty_like(csrc)
         cdst.copy_(csrc)
-    e1.record()
-    torch.cuda.synchronize()
-    copy_gbps = 5 * 2 * csrc.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del csrc, cdst
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            cdst.copy_(csrc)
+        e1.record()
+        torch.cuda.synchronize()
+        copy_gbps = 5 * 2 * csrc.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        del csrc, cdst
     if args.copy_calibration:
         # a plain copy of known size, for scaling the HBM byte counters
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
@@ -720,7 +786,8 @@ def main():
     kern = Z.timing_read()
     if Z.zp_workspace_error(ws) != Z.ZP_OK:
         raise RuntimeError("device error during the timed steps")
-    print(f"[bench] {steps} steps in {elapsed:.3f} s", file=sys.stderr, flush=True)
+    print(f"[bench] {spec.name}: {steps} steps in {elapsed:.3f} s", file=sys.stderr,
+          flush=True)
 
     hole_np = holes[warm:].cpu().numpy().astype(np.int64)
     M = (k - hole_np).clip(min=0)                      # moved rows per unit
@@ -763,9 +830,9 @@ def main():
     flops = U * (2.0 * spec.window * G * spec.head_dim * n
                  + 2.0 * spec.block_size * spec.head_dim * n)
     t_c = kernels["compress"]["avg_ms"] * 1e-3
-    mfma = {"alg_TFLOPs": round(flops / t_c / 1e12, 1),
-            "peak_TFLOPs": 2500.0 if spec.dtype == "bf16" else 157.3,
-            "frac": round(flops / t_c / 1e12 / (2500.0 if spec.dtype == "bf16" else 157.3), 4)}
+    peak_tf = 2500.0 if spec.dtype == "bf16" else 157.3
+    mfma = {"alg_TFLOPs": round(flops / t_c / 1e12, 1), "peak_TFLOPs": peak_tf,
+            "frac": round(flops / t_c / 1e12 / peak_tf, 4)}
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": steps, "warmup": warm,
@@ -785,17 +852,82 @@ def main():
         "achieved_GBps": round(gbps, 1),
         "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
         "moved_rows_mean": round(float(M.mean()), 1),
-        "copy_peak_GBps": round(copy_gbps, 1),
-        "frac_of_copy_peak": round(gbps / copy_gbps, 4),
         "roofline": roofline,
         "mfma": mfma,
         "kernels": kernels,
         # inputs come from torch's device Philox generator: record its build
         "software": {"torch": torch.__version__, "hip": torch.version.hip},
     }
-    if not args.no_cpu:
+    if copy_gbps is not None:
+        result["torch_copy_GBps"] = round(copy_gbps, 1)
+        result["frac_of_torch_copy"] = round(gbps / copy_gbps, 4)
+    if with_cpu:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(spec, wl, args.cpu_seconds)
+    del wl, globs, out, holes, batch, tables, dst_table, pool
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return result
+
+
+def _brief(res: dict) -> dict:
+    """The per-config entry of the headline line."""
+    r = res["roofline"]
+    return {"ms_per_step": res["ms_per_step"], "ms_step_median": res["ms_step_median"],
+            "tokens_per_s": res["value"], "steps": res["steps"],
+            "achieved_GBps": res["achieved_GBps"], "frac_of_peak": res["frac_of_peak"],
+            "kernel_avg_ms": res["kernels"]["compress"]["avg_ms"],
+            "kernel_frac": r["frac"], "alg_bytes_per_launch": r["alg_bytes_per_launch"],
+            "moved_rows_mean": res["moved_rows_mean"]}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the "
+              "compression path needs no collective, see the design notes on "
+              "sharding.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import kv_cache_compression_paged_amd as Z
+    from kv_cache_compression_paged_amd import synth
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    Z.lib()
+    if args.workload == "capture_8b_32L_32q":
+        run_capture(args)
+        return
+    if args.workload == "decode_8b_32L_8kv_32q":
+        run_decode(args)
+        return
+    if args.workload == "redundancy_ablation_8b":
+        run_redundancy_ablation(args)
+        return
+    if args.workload == "redundancy_sweep":
+        run_redundancy_sweep(args)
+        return
+    if args.workload == "engine_8b":
+        run_engine(args)
+        return
+    spec = synth.SPECS[args.workload]
+    if spec.compress_groups > 1:
+        print(json.dumps(run_overlap(args, spec, args.steps, args.warmup)), flush=True)
+        return
+    result = measure_compress(spec, args, args.steps, args.warmup, not args.no_cpu)
+    if args.workload == synth.EIGHT_B.name and not args.headline_only:
+        # the other workloads, driver-timed in the same run: a few steps each,
+        # one at a time (the largest pools need most of the device)
+        ks, kw = min(args.steps, 10), min(args.warmup, 3)
+        others = {}
+        for other in (synth.TINY, synth.SMALL, synth.PREFIX):
+            others[other.name] = _brief(measure_compress(other, args, ks, kw, False,
+                                                         with_copy=False))
+        ov = run_overlap(args, synth.OVERLAP, min(args.steps, 8), min(args.warmup, 2))
+        others[synth.OVERLAP.name] = {
+            "tokens_per_s": ov["value"], "steps": ov["steps"], **ov["overlap"],
+            "achieved_GBps_CD": ov["achieved_GBps"], "frac_of_peak_CD": ov["frac_of_peak"]}
+        result["other_workloads"] = others
     print(json.dumps(result), flush=True)
 
 

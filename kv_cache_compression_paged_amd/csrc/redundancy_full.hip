@@ -3,17 +3,34 @@
 // N*b cached keys, O(N^2 b^2) for N blocks, and could exhaust memory; the
 // lightning score keeps only the pairs inside a block, O(N b^2)).
 //
-// Every 16x16 tile of the n x n key Gram matrix is formed on MFMA (the same
-// fragment layout as the compression kernel: lane (j, n) holds chunk j of row
-// n, so the contraction is exact) and turned into cosines with the norms of
-// its rows and columns. Each token gets two means: over the other tokens of
-// its block (equal to the lightning score) and over all other tokens. One
-// wave owns one row tile and walks every column tile of its unit through the
-// block table; waves are independent (no LDS, no barriers).
+// The unit's n x n key Gram matrix is a dense contraction over head_dim, so
+// it runs as a tiled product on MFMA. A workgroup of 4 waves owns a panel of
+// row tiles (4 per wave for 16-byte-per-lane-chunk fragments, 2 for fp32
+// with head_dim 128); their fragments stay in registers while the unit's
+// column tiles stream past, four per step, through a 3-slot LDS ring filled
+// by direct global->LDS loads (each wave loads one tile; rows are
+// XOR-swizzled so the fragment reads hit distinct banks). One step costs
+// each wave 4 x RT tile products against one LDS read of each column tile.
+//
+// Cosines: cos(i, j) = g_ij / max(|k_i| |k_j|, 1e-8). Wherever every pair of
+// a (row tiles, column tile) step clears the clamp -- the wave's smallest
+// row norm times the tile's smallest column norm is at least 1e-8 -- the
+// row sum is taken as (1/|k_i|) * sum_j g_ij / |k_j|: one FMA per element,
+// with 1/|k_i| applied once at the end. Tiles where the clamp may bind, and
+// the diagonal tiles (which also give the same-block sums and exclude
+// j == i), take the per-element form. Each token gets two means: over the
+// other tokens of its block (equal to the lightning score) and over all
+// other tokens.
+//
+// The panels of one unit read the same column tiles, so the workgroup ids
+// are dealt to XCDs (round robin on the device) such that consecutive panels
+// of a unit share one XCD and its L2.
 #include <hip/hip_runtime.h>
 
 #include "zp_device.h"
 #include "zp_host.h"
+
+#define ZP_LDS __attribute__((address_space(3)))
 
 namespace {
 
@@ -21,7 +38,10 @@ using zpd::f32x4_t;
 using zpd::Frag;
 
 constexpr int kThreads = 256;
+constexpr int kWaves = 4;
 constexpr int kB = 16;
+constexpr int kRing = 3;
+constexpr int kXcds = 8;
 
 struct FullArgs {
   float* red_block;
@@ -29,109 +49,265 @@ struct FullArgs {
   const void* kpool;
   const int32_t* n_tokens;
   const int32_t* src_table;
-  int32_t units, L, NB, Hkv, max_blocks, n_cap, tiles_per_unit;
+  int32_t units, L, NB, Hkv, max_blocks, n_cap, panels;
   int32_t* err;
 };
 
-// squared norm of row nl of a fragment, summed over the four lanes that hold
-// its chunks (lanes nl, nl+16, nl+32, nl+48)
 template <typename E, int D>
-__device__ __forceinline__ float row_norm2(const Frag<E, D>& f) {
-  float s = f.sumsq();
-  s += zpd::shfl_xor(s, 16);
-  s += zpd::shfl_xor(s, 32);
-  return s;
+struct Geo {
+  static constexpr int kRowBytes = D * E::kBytes;          // 128, 256 or 512
+  static constexpr int kRowChunks = kRowBytes / 16;
+  static constexpr int kTileBytes = kB * kRowBytes;        // 2, 4 or 8 KiB
+  static constexpr int kLoads = kTileBytes / 1024;          // per tile and wave
+  static constexpr int kSwz = kRowChunks < 16 ? kRowChunks - 1 : 15;
+  static constexpr int RT = Frag<E, D>::kChunks <= 4 ? 4 : 2;  // row tiles per wave
+  static constexpr int kPanelTiles = kWaves * RT;
+  __device__ static constexpr int chunk_off(int row, int c) {
+    return row * kRowBytes + ((c ^ (row & kSwz)) << 4);
+  }
+};
+
+// s_waitcnt: vmcnt = n (0, 2, 4 or 8), expcnt untouched, lgkmcnt = 0.
+__device__ __forceinline__ void wait_vm_lgkm0(int n) {
+#define ZP_W(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (((N) >> 4) << 14) | (7 << 4))
+  switch (n) {
+    case 2: ZP_W(2); break;
+    case 4: ZP_W(4); break;
+    case 8: ZP_W(8); break;
+    default: ZP_W(0); break;
+  }
+#undef ZP_W
+}
+
+// LDS accesses stay in program order around a raw barrier that does not wait
+// for global->LDS loads in flight.
+__device__ __forceinline__ void raw_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0) only
+  raw_barrier();
 }
 
 template <typename E, int D>
 __global__ __launch_bounds__(kThreads) void redundancy_full_kernel(FullArgs a) {
   using FragT = Frag<E, D>;
-  constexpr int kRowBytes = D * E::kBytes;
-  const int lane = threadIdx.x & 63;
+  using GE = Geo<E, D>;
+  constexpr int RT = GE::RT;
+  __shared__ __attribute__((aligned(16))) char ring[kRing][kWaves][GE::kTileBytes];
+  __shared__ float cn2[2][kWaves][kB];   // squared norms of the step's columns
+  __shared__ float cmin[2][kWaves];      // smallest valid one per tile
+  __shared__ int tab[1024];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int jg = lane >> 4, nl = lane & 15;
-  const int wid = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  if (wid >= a.units * a.tiles_per_unit) return;   // grid padding
-  const int u = wid / a.tiles_per_unit;
-  const int rt = wid - u * a.tiles_per_unit;          // this wave's row tile
+  // the grid is a multiple of 8: block b runs on XCD b % 8, and takes logical
+  // id (b % 8) * (grid / 8) + b / 8, so consecutive ids share an XCD
+  const int per_xcd = gridDim.x / kXcds;
+  const int lid = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (lid >= a.units * a.panels) return;
+  const int u = lid / a.panels, panel = lid - u * a.panels;
   const int h = u % a.Hkv;
   const int l = (u / a.Hkv) % a.L;
   const int r = u / (a.Hkv * a.L);
   const int n = a.n_tokens[r];
   const int nt = (n + kB - 1) / kB;
-  if (n < 1 || n > a.n_cap || nt > a.max_blocks) {
-    if (lane == 0 && rt == 0) *a.err = ZP_EDEVICE;
+  if (n < 1 || n > a.n_cap || nt > a.max_blocks || nt > 1024) {
+    if (tid == 0 && panel == 0) *a.err = ZP_EDEVICE;
     return;
   }
-  if (rt >= nt) return;
-  const int32_t* tab = a.src_table + static_cast<int64_t>(r) * a.max_blocks;
+  const int tile0 = panel * GE::kPanelTiles;
+  if (tile0 >= nt) return;
+  const int32_t* src_tab = a.src_table + static_cast<int64_t>(r) * a.max_blocks;
   bool bad = false;
-  for (int j = lane; j < nt; j += 64) bad |= tab[j] < 0 || tab[j] >= a.NB;
-  if (__any(bad)) {
-    if (lane == 0) *a.err = ZP_EDEVICE;
+  for (int j = tid; j < nt; j += kThreads) {
+    const int b = src_tab[j];
+    bad |= b < 0 || b >= a.NB;
+    tab[j] = b;
+  }
+  if (__syncthreads_or(bad)) {
+    if (tid == 0) *a.err = ZP_EDEVICE;
     return;
   }
   const char* base = static_cast<const char*>(a.kpool) +
-                     (static_cast<int64_t>(l) * a.NB * a.Hkv + h) * kB * kRowBytes;
-  const int64_t block_stride = static_cast<int64_t>(a.Hkv) * kB * kRowBytes;
-  const int chunk_off = jg * (D / 4) * E::kBytes;
+                     (static_cast<int64_t>(l) * a.NB * a.Hkv + h) * GE::kTileBytes;
+  const int64_t block_stride = static_cast<int64_t>(a.Hkv) * GE::kTileBytes;
 
-  FragT rowf;
-  if (rt * kB + nl < n)
-    rowf.load(base + tab[rt] * block_stride + nl * kRowBytes + chunk_off);
-  else
-    rowf.zero();
-  // norms of the rows this lane's outputs hold (rows 4 jg + i of the tile)
-  const float rn_own = row_norm2<E, D>(rowf);
-  float rn[4];
+  // ---- this wave's row tiles: fragments and squared row norms
+  FragT A[RT];
+  float rn2[RT][4];
+  float rmin2 = INFINITY;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) rn[i] = __shfl(rn_own, 4 * jg + i, 64);
-
-  float all_sum[4] = {0.f, 0.f, 0.f, 0.f}, blk_sum[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int ct = 0; ct < nt; ++ct) {
-    FragT colf;
-    const int col = ct * kB + nl;
-    if (col < n)
-      colf.load(base + tab[ct] * block_stride + nl * kRowBytes + chunk_off);
+  for (int rt = 0; rt < RT; ++rt) {
+    const int grt = tile0 + wave * RT + rt;
+    const int row = grt * kB + nl;
+    if (grt < nt && row < n)
+      A[rt].load(base + tab[grt] * block_stride + nl * GE::kRowBytes +
+                 jg * (D / 4) * E::kBytes);
     else
-      colf.zero();
-    const float cn = row_norm2<E, D>(colf);     // norm^2 of column nl
-    const f32x4_t g = zpd::mma_rows<E, D>(rowf, colf, f32x4_t{0.f, 0.f, 0.f, 0.f});
+      A[rt].zero();
+    float own = A[rt].sumsq();
+    own += zpd::shfl_xor(own, 16);
+    own += zpd::shfl_xor(own, 32);
+    if (grt < nt && row < n) rmin2 = fminf(rmin2, own);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = rt * kB + 4 * jg + i;
-      const float c = (col < n && row != col)
-                          ? g[i] * __builtin_amdgcn_rsqf(fmaxf(rn[i] * cn, 1e-16f))
-                          : 0.f;
-      all_sum[i] += c;
-      if (ct == rt) blk_sum[i] += c;
+    for (int i = 0; i < 4; ++i) rn2[rt][i] = __shfl(own, 4 * jg + i, 64);
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) rmin2 = fminf(rmin2, zpd::shfl_xor(rmin2, o));
+
+  // ---- column sweep: step s covers column tiles 4s .. 4s+3
+  int src_off[GE::kLoads];
+#pragma unroll
+  for (int e = 0; e < GE::kLoads; ++e) {
+    const int sidx = e * 64 + lane;
+    const int row = sidx / GE::kRowChunks, pos = sidx % GE::kRowChunks;
+    src_off[e] = row * GE::kRowBytes + ((pos ^ (row & GE::kSwz)) << 4);
+  }
+  int frag_off[FragT::kChunks];
+#pragma unroll
+  for (int c = 0; c < FragT::kChunks; ++c)
+    frag_off[c] = GE::chunk_off(nl, jg * FragT::kChunks + c);
+  auto issue = [&](int s) {  // this wave's column tile of step s
+    const int ct = 4 * s + wave;
+    if (ct >= nt) return;
+    const char* src = base + tab[ct] * block_stride;
+    char* dst = ring[s % kRing][wave];
+#pragma unroll
+    for (int e = 0; e < GE::kLoads; ++e)
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + src_off[e]),
+                                       (ZP_LDS void*)(dst + e * 1024), 16, 0, 0);
+  };
+  auto read_frag = [&](FragT& f, int slot, int c) {
+    const char* p = ring[slot][c];
+#pragma unroll
+    for (int k = 0; k < FragT::kChunks; ++k)
+      f.v[k] = *reinterpret_cast<const zpd::u32x4_t*>(p + frag_off[k]);
+  };
+
+  float fact[RT][4], exact[RT][4], blk[RT][4];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fact[rt][i] = exact[rt][i] = blk[rt][i] = 0.f;
+
+  const int nsteps = (nt + 3) / 4;
+  issue(0);
+  for (int s = 0; s < nsteps; ++s) {
+    // the slot step s+1 fills was last read in step s-2, which every wave
+    // finished before the barriers of step s-1
+    const bool more = s + 1 < nsteps && 4 * (s + 1) + wave < nt;
+    if (s + 1 < nsteps) issue(s + 1);
+    wait_vm_lgkm0(more ? GE::kLoads : 0);
+    raw_barrier();  // step s's tiles have landed (every wave waited on its own)
+    const int slot = s % kRing;
+    {
+      const int ct = 4 * s + wave;
+      if (ct < nt) {
+        FragT f;
+        read_frag(f, slot, wave);
+        const bool ok = ct * kB + nl < n;
+        float sq = ok ? f.sumsq() : 0.f;
+        sq += zpd::shfl_xor(sq, 16);
+        sq += zpd::shfl_xor(sq, 32);
+        float mn = ok ? sq : INFINITY;
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) mn = fminf(mn, zpd::shfl_xor(mn, o));
+        if (jg == 0) cn2[s & 1][wave][nl] = sq;
+        if (lane == 0) cmin[s & 1][wave] = mn;
+      }
+    }
+    lds_barrier();
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int ct = 4 * s + c;
+      if (ct >= nt) break;
+      const int col = ct * kB + nl;
+      const bool ok = col < n;
+      FragT f;
+      read_frag(f, slot, c);
+      if (!ok) f.zero();
+      const float c2 = cn2[s & 1][c][nl];
+      const bool safe = rmin2 * cmin[s & 1][c] >= 1e-16f;
+      const float cinv = (ok && safe) ? __builtin_amdgcn_rsqf(c2) : 0.f;
+      f32x4_t g[RT];
+      if constexpr (E::kBytes == 2) {
+        // chunk-major: the RT accumulation chains interleave
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) g[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < FragT::kChunks; ++k)
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+            g[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(zpd::bf16x8_t, A[rt].v[k]),
+                __builtin_bit_cast(zpd::bf16x8_t, f.v[k]), g[rt], 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+          g[rt] = zpd::mma_rows<E, D>(A[rt], f, f32x4_t{0.f, 0.f, 0.f, 0.f});
+      }
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const int grt = tile0 + wave * RT + rt;
+        if (grt >= nt) continue;
+        if (ct != grt && safe) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) fact[rt][i] = fmaf(g[rt][i], cinv, fact[rt][i]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = grt * kB + 4 * jg + i;
+            const float cv = (ok && row != col)
+                                 ? g[rt][i] * __builtin_amdgcn_rsqf(fmaxf(rn2[rt][i] * c2, 1e-16f))
+                                 : 0.f;
+            exact[rt][i] += cv;
+            if (ct == grt) blk[rt][i] += cv;
+          }
+        }
+      }
     }
   }
-  // sum over the 16 columns of the tile (lanes of one row group)
+
+  // ---- row sums over the 16 columns a lane group holds, then the means
+  const int64_t urow = static_cast<int64_t>(u) * a.n_cap;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      all_sum[i] += zpd::shfl_xor(all_sum[i], o);
-      blk_sum[i] += zpd::shfl_xor(blk_sum[i], o);
-    }
-  if (nl == 0) {
-    const int cnt = min(kB, n - rt * kB);
-    const int64_t urow = static_cast<int64_t>(u) * a.n_cap;
+  for (int rt = 0; rt < RT; ++rt) {
+    const int grt = tile0 + wave * RT + rt;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row = rt * kB + 4 * jg + i;
-      if (row >= n) continue;
-      a.red_block[urow + row] = cnt >= 2 ? blk_sum[i] / (cnt - 1) : 0.f;
-      if (a.red_all) a.red_all[urow + row] = n >= 2 ? all_sum[i] / (n - 1) : 0.f;
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        fact[rt][i] += zpd::shfl_xor(fact[rt][i], o);
+        exact[rt][i] += zpd::shfl_xor(exact[rt][i], o);
+        blk[rt][i] += zpd::shfl_xor(blk[rt][i], o);
+      }
+      const int row = grt * kB + 4 * jg + i;
+      if (nl == 0 && grt < nt && row < n) {
+        const float rinv = rn2[rt][i] > 0.f ? __builtin_amdgcn_rsqf(rn2[rt][i]) : 0.f;
+        const float all = fmaf(fact[rt][i], rinv, exact[rt][i]);
+        const int cnt = min(kB, n - grt * kB);
+        a.red_block[urow + row] = cnt >= 2 ? blk[rt][i] / (cnt - 1) : 0.f;
+        if (a.red_all) a.red_all[urow + row] = n >= 2 ? all / (n - 1) : 0.f;
+      }
     }
   }
 }
 
 template <typename E, int D>
-zp_status launch_full(const FullArgs& a, unsigned waves, void* stream) {
-  const unsigned grid = (waves + kThreads / 64 - 1) / (kThreads / 64);
-  hipLaunchKernelGGL((redundancy_full_kernel<E, D>), dim3(grid), dim3(kThreads), 0,
-                     static_cast<hipStream_t>(stream), a);
+zp_status launch_full(FullArgs a, void* stream) {
+  a.panels = ((a.n_cap + kB - 1) / kB + Geo<E, D>::kPanelTiles - 1) / Geo<E, D>::kPanelTiles;
+  const int64_t work = static_cast<int64_t>(a.units) * a.panels;
+  const int64_t grid = (work + kXcds - 1) / kXcds * kXcds;
+  if (grid > (1ll << 31) - 1)
+    return zp::fail(ZP_EINVAL, "all-pairs redundancy: %lld workgroups",
+                    static_cast<long long>(grid));
+  hipLaunchKernelGGL((redundancy_full_kernel<E, D>), dim3(static_cast<unsigned>(grid)),
+                     dim3(kThreads), 0, static_cast<hipStream_t>(stream), a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess)
     return zp::fail(ZP_EHIP, "all-pairs redundancy launch: %s", hipGetErrorString(e));
@@ -157,18 +333,14 @@ zp_status launch_redundancy_full(const CompressGeom& g, const zp_kv_pool& pool,
   a.Hkv = g.Hkv;
   a.max_blocks = g.max_blocks;
   a.n_cap = g.n_cap;
-  a.tiles_per_unit = (g.n_cap + kB - 1) / kB;
+  a.panels = 0;
   a.err = err;
-  const int64_t waves64 = static_cast<int64_t>(a.units) * a.tiles_per_unit;
-  if (waves64 > (1ll << 31) - 4)
-    return fail(ZP_EINVAL, "all-pairs redundancy: %lld waves", static_cast<long long>(waves64));
-  const unsigned waves = static_cast<unsigned>(waves64);
   if (g.dtype == ZP_BF16) {
-    if (g.d == 128) return launch_full<zpd::BF16, 128>(a, waves, stream);
-    if (g.d == 64) return launch_full<zpd::BF16, 64>(a, waves, stream);
+    if (g.d == 128) return launch_full<zpd::BF16, 128>(a, stream);
+    if (g.d == 64) return launch_full<zpd::BF16, 64>(a, stream);
   } else {
-    if (g.d == 128) return launch_full<zpd::F32, 128>(a, waves, stream);
-    if (g.d == 64) return launch_full<zpd::F32, 64>(a, waves, stream);
+    if (g.d == 128) return launch_full<zpd::F32, 128>(a, stream);
+    if (g.d == 64) return launch_full<zpd::F32, 64>(a, stream);
   }
   return fail(ZP_EUNSUPPORTED, "all-pairs redundancy: head_dim %d", g.d);
 }
