@@ -14,25 +14,6 @@
 
 namespace zp {
 
-namespace {
-thread_local char g_msg[512] = "";
-}
-
-void set_error(const char* fmt, ...) {
-  va_list ap;
-  va_start(ap, fmt);
-  vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
-  va_end(ap);
-}
-
-zp_status fail(zp_status code, const char* fmt, ...) {
-  va_list ap;
-  va_start(ap, fmt);
-  vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
-  va_end(ap);
-  return code;
-}
-
 // ------------------------------------------------------------------ timing
 namespace {
 struct Pending {
@@ -462,22 +443,6 @@ zp_status zp_timing_read(int32_t* launches, double* total_ms) {
   g_pending.clear();
   return st;
 }
-
-const char* zp_status_str(zp_status s) {
-  switch (s) {
-    case ZP_OK: return "ZP_OK";
-    case ZP_EINVAL: return "ZP_EINVAL";
-    case ZP_EUNSUPPORTED: return "ZP_EUNSUPPORTED";
-    case ZP_EWORKSPACE: return "ZP_EWORKSPACE";
-    case ZP_ENOSPACE: return "ZP_ENOSPACE";
-    case ZP_EHIP: return "ZP_EHIP";
-    case ZP_EDEVICE: return "ZP_EDEVICE";
-    case ZP_ESYNC: return "ZP_ESYNC";
-    default: return "ZP_UNKNOWN";
-  }
-}
-
-const char* zp_last_error(void) { return g_msg; }
 
 const char* zp_version(void) { return "zipage-gfx950 0.1"; }
 
