@@ -53,7 +53,10 @@ typedef int32_t zp_status;
 #define ZP_EDEVICE      -6  /* a kernel found a bad device table entry       */
 #define ZP_ESYNC        -7  /* workgroups of a split unit stopped waiting on
                                each other (bounded wait passed); the call's
-                               outputs are incomplete                        */
+                               outputs are incomplete: every unit's K/V rows
+                               and global row are either fully compacted or
+                               untouched, but which is not reported, so the
+                               batch's requests must be prefilled again     */
 
 /* element types */
 #define ZP_F32  0

@@ -124,13 +124,15 @@ __device__ __forceinline__ uint32_t xload32(const uint32_t* p) {
 }
 
 // Polls until ready() holds in every lane of the wave (ready() loads what it
-// still lacks). Returns false once `limit` polls found it unready or another
-// workgroup raised the abort flag; then the flag is raised here too.
+// still lacks). Returns false once `limit` polls found it unready or, with
+// honor_abort, another workgroup raised the abort flag; then the flag is
+// raised here too.
 template <typename F>
-__device__ __forceinline__ bool wave_poll(F&& ready, uint32_t* abort_flag, int limit) {
+__device__ __forceinline__ bool wave_poll(F&& ready, uint32_t* abort_flag, int limit,
+                                          bool honor_abort = true) {
   for (int it = 0;; ++it) {
     if (__all(ready())) return true;
-    if (it >= limit || xload32(abort_flag) != 0u) {
+    if (it >= limit || (honor_abort && xload32(abort_flag) != 0u)) {
       __hip_atomic_store(abort_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return false;
     }
@@ -731,6 +733,13 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
         cw[e] = 0;
       }
       const uint32_t tmask = tag & kTagMask;
+      // After posting, only this group's own words decide (its own bounded
+      // wait, not another group's abort): a sibling that holds every
+      // candidate may already be writing into this part's slice, so giving
+      // up because some other group stopped would leave the unit half
+      // compacted. If every part posted, every part sees every word and
+      // completes the unit; if one did not, no part holds all of them and
+      // none writes.
       const bool ok = wave_poll([&]() {
 #pragma unroll
         for (int e = 0; e < kCandPer; ++e) {
@@ -753,7 +762,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
           all &= have[e];
         }
         return all;
-      }, abort_flag, a.spin_limit);
+      }, abort_flag, a.spin_limit, /*honor_abort=*/false);
       if (wg_or(!ok, scratch)) {
         if (tid == 0) *a.err = ZP_ESYNC;
         return;

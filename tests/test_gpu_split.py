@@ -275,3 +275,88 @@ def test_wait_limit_reports_esync_and_the_workspace_recovers(monkeypatch):
     assert torch.equal(keep1, keep2)
     assert torch.equal(k1, k2) and torch.equal(v1, v2)
     _say("[split] ZP_ESYNC reported; the workspace serves the next call unchanged")
+
+
+def test_split_schedule_beside_decode_on_another_stream():
+    """The two-stream case on the split-unit schedule: 8 query-slot holders
+    (4 layers x 8 KV heads of the 8B-like layout) compress on stream C with
+    ZP_SPLIT_UNITS and the global update fused, while the other 24 requests
+    decode one token on stream D, so the persistent split grid shares the
+    device with decode workgroups. Every compressed unit is checked (keep =
+    top k of its own scores, rows against an untouched copy, global rows bit
+    for bit), 6 of them against the oracle, and 16 decode pairs against the
+    oracle's attention."""
+    import oracle as O
+    from tests import fullsize as F
+    spec = synth.scaled(synth.OVERLAP, requests=32, layers=4, groups=4,
+                        compress_groups=4, pool_blocks=32 * 256)
+    dev = "cuda"
+    per = 8
+    wl = synth.make(spec, device=dev, slots=per)
+    L, H, b = spec.layers, spec.kv_heads, spec.block_size
+    n, k = spec.n_tokens, spec.keep
+    G = spec.q_heads // H
+    grp, rest = np.arange(per), np.arange(per, spec.requests)
+    tab_c = torch.from_numpy(np.ascontiguousarray(wl.tables[grp])).to(dev)
+    tab_d = torch.from_numpy(np.ascontiguousarray(wl.tables[rest])).to(dev)
+    rng = np.random.default_rng(41)
+    lens = rng.integers(k + 1, n, size=rest.size).astype(np.int32)
+    q = synth.decode_queries(spec, rest.size, dev, 42)
+    zparams, oparams = P._params_for(spec, SPLIT | Z.ZP_UPDATE_GLOBAL)
+    pool = Z.make_pool(wl.k_pool, wl.v_pool)
+    batch = Z.DeviceBatch(
+        slot=torch.arange(per, dtype=torch.int32, device=dev),
+        n_tokens=torch.full((per,), n, dtype=torch.int32, device=dev),
+        src_table=tab_c, dst_table=tab_c.clone(),
+        n_pinned=torch.zeros(per, dtype=torch.int32, device=dev),
+        num_slots=per, n_cap=wl.n_cap)
+    Uc = per * L * H
+    out = Z.alloc_outputs(Uc, k, wl.n_cap, dev, debug=True)
+    ws = Z.alloc_workspace(pool, zparams, per, dev)
+    assert ws.numel() * ws.element_size() > 256          # the split schedule runs
+    k0, v0, g0 = wl.k_pool.clone(), wl.v_pool.clone(), wl.global_scores.clone()
+    qwin = synth.raw_numpy(wl.q_window)
+    dec = torch.full((rest.size, L, spec.q_heads, spec.head_dim), float("nan"),
+                     dtype=torch.float32, device=dev)
+    sc, sd = torch.cuda.Stream(), torch.cuda.Stream()
+    ready = torch.cuda.Event()
+    ready.record(torch.cuda.current_stream())
+    sc.wait_event(ready)
+    sd.wait_event(ready)
+    _say(f"[split] two streams: {Uc} units split on C, {rest.size} requests decode on D")
+    Z.zp_compress(pool, batch, wl.q_window, wl.global_scores, zparams, out, ws, sc)
+    Z.zp_paged_decode(dec, q, pool, tab_d, torch.from_numpy(lens).to(dev), zparams, sd)
+    torch.cuda.synchronize()
+    assert Z.zp_workspace_error(ws) == Z.ZP_OK
+    F.check_keep_is_topk_of_own_scores(out.keep_idx, out.score, n)
+    F.check_global_rows(wl.global_scores, g0, out.keep_idx, out.attn, range(per), L, H)
+    F.check_rows_against_copy(wl.k_pool, k0, tab_c, batch.dst_table, out.keep_idx, n,
+                              spec.n_max, in_place=True, what="K")
+    F.check_rows_against_copy(wl.v_pool, v0, tab_c, batch.dst_table, out.keep_idx, n,
+                              spec.n_max, in_place=True, what="V")
+    hk = synth.raw_numpy(k0)
+    for u in sorted(set(int(x) for x in rng.choice(Uc, 6, replace=False)) | {0, Uc - 1}):
+        r, l, h = u // (L * H), (u // H) % L, u % H
+        keys = O.widen(O.gather_rows(hk, wl.tables[r], l, h, n, b), spec.dtype)
+        ur = O.score_unit(O.widen(qwin[r, l, :, h * G:(h + 1) * G], spec.dtype), keys,
+                          g0[r, l, h].cpu().numpy().astype(np.float64), n, 0, oparams)
+        ga = out.attn[u, :n].cpu().numpy().astype(np.float64)
+        assert np.all(np.abs(ga - ur.attn) <= P.ATTN_RTOL * np.abs(ur.attn) + P.ATTN_ATOL)
+        diff = set(out.keep_idx[u].cpu().numpy().tolist()) ^ set(ur.keep.tolist())
+        fin = np.isfinite(ur.score)
+        tau = min(float(ur.score[t]) for t in ur.keep if fin[t])
+        assert all(abs(ur.score[t] - tau) <= P.BAND for t in diff)
+    qh = synth.raw_numpy(q)
+    got = dec.cpu().numpy().astype(np.float64)
+    hv = synth.raw_numpy(v0)
+    for i in rng.choice(rest.size, 4, replace=False):
+        for l in range(L):
+            r = int(rest[i])
+            for h in range(H):
+                kr = O.gather_rows(hk, wl.tables[r], l, h, int(lens[i]), b)
+                vr = O.gather_rows(hv, wl.tables[r], l, h, int(lens[i]), b)
+                want = O.decode_attention(O.widen(qh[i, l, h * G:(h + 1) * G], spec.dtype),
+                                          O.widen(kr, spec.dtype), O.widen(vr, spec.dtype))
+                err = np.abs(got[i, l, h * G:(h + 1) * G] - want)
+                assert np.all(err <= 1e-4 * np.abs(want) + 1e-5), (r, l, h, err.max())
+    _say("[split] two streams: compressed units and decode pairs match")
