@@ -105,6 +105,7 @@ KERNEL_SOURCES = {
     "global_update": ["global_update.hip", "zp_device.h"],
     "paged_decode": ["decode.hip", "zp_device.h"],
     "capture": ["capture.hip", "zp_device.h"],
+    "redundancy_full": ["redundancy_full.hip", "zp_device.h"],
 }
 
 
@@ -532,7 +533,8 @@ def run_redundancy_ablation(args):
                      "achieved": round(flops_full / (t_full * 1e-3) / 1e12, 1),
                      "peak": 2500.0, "unit": "TFLOP/s",
                      "frac": round(flops_full / (t_full * 1e-3) / 1e12 / 2500.0, 4),
-                     "traffic": None, "alg_bytes_per_launch": None},
+                     "traffic": traffic_from_profile("redundancy_full", "redundancy_ablation_8b"),
+                     "alg_flops_per_launch": flops_full},
     }), flush=True)
 
 
