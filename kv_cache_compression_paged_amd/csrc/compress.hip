@@ -45,6 +45,8 @@
 // exponentials (fenced with sched_barrier) instead of all before them.
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
+
 #include "zp_device.h"
 #include "zp_host.h"
 
@@ -55,9 +57,6 @@ namespace {
 using zpd::f32x4_t;
 using zpd::Frag;
 
-constexpr int kThreads = 512;
-constexpr int kWaves = 8;
-constexpr int kQuarters = 4;
 constexpr int kB = 16;  // block size b (one key tile = one block)
 
 struct ScoreArgs {
@@ -82,16 +81,20 @@ struct ScoreArgs {
   float w_attn, w_global, w_red, sl2;  // sl2 = softmax scale * log2(e)
 };
 
-// Ring slots per quarter: about 112 KiB of LDS, 4 to 8 slots.
-#ifndef ZP_RING_KIB
-#define ZP_RING_KIB 112
-#endif
+// Workgroup shapes. KG key groups of two waves each (one per row half):
+// KG = 4 is one 8-wave workgroup per CU with a 112 KiB key ring; KG = 2 is a
+// 4-wave workgroup with a 56 KiB ring, so that two of them (two units) share
+// a CU and one's latency-bound phases (set-up, select, compaction) overlap
+// the other's sweeps.
+constexpr int threads_of(int kg) { return 128 * kg; }
+// Ring slots per key group: 4 to 8 slots in about 28 KiB per group.
 template <typename E, int D>
 constexpr int default_slots() {
-  constexpr int n = ZP_RING_KIB * 1024 / (kQuarters * 16 * D * E::kBytes);
+  constexpr int n = 28 * 1024 / (16 * D * E::kBytes);
   return n > 8 ? 8 : (n < 4 ? 4 : n);
 }
 constexpr int kLongSlots = 4;
+constexpr size_t kLdsPerCu = 160 * 1024;
 
 // s_waitcnt with vmcnt = n (0..28 or 32), expcnt untouched, lgkmcnt = 0.
 __device__ __forceinline__ void wait_vm_lgkm0(int n) {
@@ -138,8 +141,12 @@ struct TileGeom {
   }
 };
 
-template <typename E, int D, int RT, int NS>
-__global__ __launch_bounds__(kThreads) void compress_kernel(ScoreArgs a) {
+template <typename E, int D, int RT, int NS, int KG>
+__global__ __launch_bounds__(threads_of(KG)) __attribute__((amdgpu_waves_per_eu(2)))
+void compress_kernel(ScoreArgs a) {
+  constexpr int kQuarters = KG;            // key groups: block kt goes to group kt mod KG
+  constexpr int kWaves = 2 * KG;           // two row halves per group
+  constexpr int kThreads = threads_of(KG);
   using FragT = Frag<E, D>;
   using TG = TileGeom<E, D, NS>;
   constexpr int kRows = RT * 16;
@@ -165,7 +172,7 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(ScoreArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int kq = wave & 3, rg = wave >> 2;
+  const int kq = wave % kQuarters, rg = wave / kQuarters;
   const int jg = lane >> 4, nl = lane & 15;
   const int u = blockIdx.x;
   const int h = u % a.Hkv;
@@ -853,16 +860,16 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(ScoreArgs a) {
   }
 }
 
-template <typename E, int D, int RT, int NS>
+template <typename E, int D, int RT, int NS, int KG>
 zp_status launch_one(const zp::CompressGeom& g, const ScoreArgs& args,
                      void* stream) {
   const size_t dyn = static_cast<size_t>(g.n_cap) * sizeof(float);
-  auto kern = compress_kernel<E, D, RT, NS>;
+  auto kern = compress_kernel<E, D, RT, NS, KG>;
   hipFuncAttributes fa;
   hipError_t e = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(kern));
   if (e != hipSuccess)
     return zp::fail(ZP_EHIP, "score kernel attributes: %s", hipGetErrorString(e));
-  if (fa.sharedSizeBytes + dyn > 160 * 1024)
+  if (fa.sharedSizeBytes + dyn > kLdsPerCu)
     return zp::fail(ZP_EUNSUPPORTED, "n_cap %d: %zu bytes of token scores do not fit "
                     "beside %zu bytes of key ring in LDS", g.n_cap, dyn,
                     static_cast<size_t>(fa.sharedSizeBytes));
@@ -872,7 +879,7 @@ zp_status launch_one(const zp::CompressGeom& g, const ScoreArgs& args,
   if (e != hipSuccess)
     return zp::fail(ZP_EHIP, "score kernel attribute: %s", hipGetErrorString(e));
   const unsigned units = static_cast<unsigned>(g.R) * g.L * g.Hkv;
-  hipLaunchKernelGGL(kern, dim3(units), dim3(kThreads), dyn,
+  hipLaunchKernelGGL(kern, dim3(units), dim3(threads_of(KG)), dyn,
                      static_cast<hipStream_t>(stream), args);
   e = hipGetLastError();
   if (e != hipSuccess)
@@ -880,21 +887,55 @@ zp_status launch_one(const zp::CompressGeom& g, const ScoreArgs& args,
   return ZP_OK;
 }
 
-// The default ring when the token rows fit beside it, else the 4-slot ring.
+template <typename E, int D, int RT, int NS, int KG>
+size_t lds_bytes(const zp::CompressGeom& g, zp_status* st) {
+  hipFuncAttributes fa;
+  const hipError_t e = hipFuncGetAttributes(
+      &fa, reinterpret_cast<const void*>(compress_kernel<E, D, RT, NS, KG>));
+  if (e != hipSuccess) {
+    *st = zp::fail(ZP_EHIP, "score kernel attributes: %s", hipGetErrorString(e));
+    return 0;
+  }
+  *st = ZP_OK;
+  return fa.sharedSizeBytes + static_cast<size_t>(g.n_cap) * sizeof(float);
+}
+
+// Which workgroup shape a launch takes: 0 = by the rule below, 2 or 4 =
+// that many key groups (the environment variable ZIPAGE_KEY_GROUPS, read at
+// each launch, so that tests can run both shapes on one input).
+int forced_key_groups() {
+  const char* v = std::getenv("ZIPAGE_KEY_GROUPS");
+  if (!v) return 0;
+  const int kg = std::atoi(v);
+  return kg == 2 || kg == 4 ? kg : 0;
+}
+
+// Two units per CU (KG = 2) when a unit's keys are at most 512 KiB and the
+// workgroup fits in half of a CU's LDS; otherwise one 8-wave workgroup per
+// CU (KG = 4) with the default ring, or the 4-slot ring when the token rows
+// do not fit beside it. The column sweep re-reads a unit's keys, mostly
+// from the last-level cache while every CU's units fit in it (256 MB): two
+// units of 512 KiB per CU are 256 MB across 256 CUs, larger units would
+// spill and are slower with two per CU than with one (measured).
 template <typename E, int D, int RT>
 zp_status launch_ring(const zp::CompressGeom& g, const ScoreArgs& args,
                       void* stream) {
   constexpr int ns = default_slots<E, D>();
-  if constexpr (ns > kLongSlots) {
-    hipFuncAttributes fa;
-    const hipError_t e = hipFuncGetAttributes(
-        &fa, reinterpret_cast<const void*>(compress_kernel<E, D, RT, ns>));
-    if (e != hipSuccess)
-      return zp::fail(ZP_EHIP, "score kernel attributes: %s", hipGetErrorString(e));
-    if (fa.sharedSizeBytes + static_cast<size_t>(g.n_cap) * sizeof(float) > 160 * 1024)
-      return launch_one<E, D, RT, kLongSlots>(g, args, stream);
+  const int forced = forced_key_groups();
+  zp_status st = ZP_OK;
+  const bool small_keys = static_cast<size_t>(g.n_cap) * D * E::kBytes <= 512 * 1024;
+  if (forced == 2 || (forced == 0 && small_keys)) {
+    const size_t lds2 = lds_bytes<E, D, RT, ns, 2>(g, &st);
+    if (st != ZP_OK) return st;
+    if (lds2 <= kLdsPerCu / 2 || (forced == 2 && lds2 <= kLdsPerCu))
+      return launch_one<E, D, RT, ns, 2>(g, args, stream);
   }
-  return launch_one<E, D, RT, ns>(g, args, stream);
+  if constexpr (ns > kLongSlots) {
+    const size_t lds4 = lds_bytes<E, D, RT, ns, 4>(g, &st);
+    if (st != ZP_OK) return st;
+    if (lds4 > kLdsPerCu) return launch_one<E, D, RT, kLongSlots, 4>(g, args, stream);
+  }
+  return launch_one<E, D, RT, ns, 4>(g, args, stream);
 }
 
 // Window rows are padded to 16, 32, 64, 128 or 192 and split between the

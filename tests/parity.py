@@ -198,7 +198,8 @@ def run_case(case: Case, device: str = "cuda") -> Result:
     out = Z.alloc_outputs(U, k, dev.n_cap, device, debug=True)
     ws = Z.alloc_workspace(pool, zparams, R, device)
     Z.zp_compress(pool, dev, wl.q_window, glob, zparams, out, ws)
-    Z.zp_update_global(glob, pool, dev, out, zparams)
+    if not (case.flags & Z.ZP_UPDATE_GLOBAL):   # else the kernel updated the rows
+        Z.zp_update_global(glob, pool, dev, out, zparams)
     torch.cuda.synchronize()
     err = Z.zp_workspace_error(ws)
     if err != Z.ZP_OK:

@@ -127,6 +127,41 @@ def test_prefix_targets_with_block_manager():
            "shared prefix -> target blocks (plans from zp_bm)")
 
 
+# The launcher runs units of at most 512 KiB of keys as two 4-wave
+# workgroups per CU (2 key groups) and larger ones as one 8-wave workgroup
+# (4 key groups); ZIPAGE_KEY_GROUPS forces either, so both workgroup shapes
+# are compared with the oracle on the same inputs.
+SHAPE_CASES = [
+    ("tiny fp32", lambda: P.Case(synth.TINY)),
+    ("192 window rows", lambda: P.Case(SMALL_MODEL)),
+    ("near duplicates", lambda: P.Case(EIGHT_B)),
+    ("non-causal", lambda: P.Case(EIGHT_B, flags=Z.ZP_NONCAUSAL)),
+    ("protected window", lambda: P.Case(EIGHT_B, flags=Z.ZP_PROTECT_WINDOW)),
+    ("bf16 d=64", lambda: P.Case(D64)),
+    ("fp32 d=128", lambda: P.Case(F32_D128)),
+    ("overshoot", lambda: P.Case(synth.scaled(EIGHT_B, requests=3, pool_blocks=112 + 12),
+                                 n_tokens=[EIGHT_B.n_tokens + e for e in (5, 16, 37)],
+                                 max_blocks=EIGHT_B.n_max + 3)),
+    ("shared prefix", lambda: P.Case(PREFIX, use_block_manager=True)),
+    ("fused update", lambda: P.Case(EIGHT_B, flags=Z.ZP_UPDATE_GLOBAL)),
+]
+
+
+@pytest.mark.parametrize("kg", ["2", "4"], ids=["2-groups", "4-groups"])
+@pytest.mark.parametrize("label,make", SHAPE_CASES, ids=[c[0] for c in SHAPE_CASES])
+def test_both_workgroup_shapes(kg, label, make, monkeypatch):
+    monkeypatch.setenv("ZIPAGE_KEY_GROUPS", kg)
+    _check(make(), f"{label}, {kg} key groups")
+
+
+@pytest.mark.parametrize("kg", ["2", "4"], ids=["2-groups", "4-groups"])
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shapes_both_workgroup_shapes(kg, seed, monkeypatch):
+    monkeypatch.setenv("ZIPAGE_KEY_GROUPS", kg)
+    case = _random_case(100 + seed)
+    _check(case, f"random shape {100 + seed}, flags {case.flags}, {kg} key groups")
+
+
 @pytest.mark.parametrize("flags", [0, Z.ZP_SPLIT_UNITS], ids=["one-workgroup", "split-units"])
 def test_device_table_errors_reject_only_their_units(flags):
     """A block id outside the pool (request 1) and a token count below the
