@@ -54,8 +54,12 @@ METRIC = "KV tokens compressed/sec + achieved HBM GB/s (frac of peak), 1 MI355X"
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup-seconds", type=float, default=0.0,
+                    help="after the --warmup steps, keep taking untimed steps until "
+                         "this many seconds of warm-up have passed (compression "
+                         "workloads; 0: exactly --warmup steps)")
     ap.add_argument("--workload", default="8b_32L_8kv_32q_N4096")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
@@ -674,9 +678,12 @@ def run_engine(args):
 
 
 def measure_compress(spec, args, steps: int, warm: int, with_cpu: bool,
-                     with_copy: bool = True) -> dict:
+                     with_copy: bool = True, warm_min_s: float = 0.0) -> dict:
     """Times `steps` compression steps of one workload and returns its JSON
-    record (the device memory of the workload is released on return)."""
+    record (the device memory of the workload is released on return).
+    After the `warm` warm-up steps, more untimed steps run until `warm_min_s`
+    seconds of warm-up have passed (0: exactly `warm`): the device takes a
+    few hundred milliseconds of this load to reach its steady clocks."""
     import torch
     import kv_cache_compression_paged_amd as Z
     from kv_cache_compression_paged_amd import synth
@@ -760,16 +767,33 @@ def measure_compress(spec, args, steps: int, warm: int, with_cpu: bool,
         torch.cuda.synchronize()
         del src, dst
 
-    def step(i):
+    def step(i, glob=None):
+        glob = globs[i] if glob is None else glob
         out.first_hole = holes[i]
-        Z.zp_compress(pool, batch, wl.q_window, globs[i], params, out, ws,
+        Z.zp_compress(pool, batch, wl.q_window, glob, params, out, ws,
                       stream)
         if args.separate_update:
-            Z.zp_update_global(globs[i], pool, batch, out, params, stream)
+            Z.zp_update_global(glob, pool, batch, out, params, stream)
 
+    t_w = time.perf_counter()
     for i in range(warm):
         step(i)
     torch.cuda.synchronize()
+    extra = 0
+    if warm_min_s > 0:
+        # Extra warm-up steps must leave the pool as the timed steps expect
+        # it (in place, every step compacts the previous step's result, and
+        # hundreds of them would pile up stale tail copies and shift the
+        # holes): global rows of 1e6 below k and 0 from k on make every unit
+        # evict exactly its tail, so it sweeps and selects but moves no row.
+        # (The update keeps that pattern: 1e6 + attn below k, 0 after.)
+        g_warm = torch.zeros_like(globs[0])
+        g_warm[..., :k] = 1e6
+        while time.perf_counter() - t_w < warm_min_s and extra < 1000:
+            step(0, g_warm)
+            torch.cuda.synchronize()
+            extra += 1
+        del g_warm
     if Z.zp_workspace_error(ws) != Z.ZP_OK:
         raise RuntimeError("device error during warm-up")
     Z.timing_read()  # drop anything recorded before
@@ -837,7 +861,7 @@ def measure_compress(spec, args, steps: int, warm: int, with_cpu: bool,
             "frac": round(flops / t_c / 1e12 / peak_tf, 4)}
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s",
-        "n_gpus": 1, "steps": steps, "warmup": warm,
+        "n_gpus": 1, "steps": steps, "warmup": warm + extra,
         "ms_per_step": round(ms_step, 3),
         "ms_step_median": round(float(np.median(step_ms)), 3),
         "ms_step_min": round(float(step_ms.min()), 3), "higher_is_better": True,
@@ -876,7 +900,7 @@ def _brief(res: dict) -> dict:
     """The per-config entry of the headline line."""
     r = res["roofline"]
     return {"ms_per_step": res["ms_per_step"], "ms_step_median": res["ms_step_median"],
-            "tokens_per_s": res["value"], "steps": res["steps"],
+            "tokens_per_s": res["value"], "steps": res["steps"], "warmup": res["warmup"],
             "achieved_GBps": res["achieved_GBps"], "frac_of_peak": res["frac_of_peak"],
             "kernel_avg_ms": res["kernels"]["compress"]["avg_ms"],
             "kernel_frac": r["frac"], "alg_bytes_per_launch": r["alg_bytes_per_launch"],
@@ -916,15 +940,17 @@ def main():
     if spec.compress_groups > 1:
         print(json.dumps(run_overlap(args, spec, args.steps, args.warmup)), flush=True)
         return
-    result = measure_compress(spec, args, args.steps, args.warmup, not args.no_cpu)
+    result = measure_compress(spec, args, args.steps, args.warmup, not args.no_cpu,
+                              warm_min_s=args.warmup_seconds)
     if args.workload == synth.EIGHT_B.name and not args.headline_only:
-        # the other workloads, timed in the same run: a few steps each,
-        # one at a time (the largest pools need most of the device)
-        ks, kw = min(args.steps, 10), min(args.warmup, 3)
+        # the other workloads, timed in the same run: up to 20 steps
+        # each after at least 0.3 s of their own warm-up steps, one at a time
+        # (the largest pools need most of the device)
+        ks, kw = min(args.steps, 20), min(args.warmup, 5)
         others = {}
         for other in (synth.TINY, synth.SMALL, synth.PREFIX):
             others[other.name] = _brief(measure_compress(other, args, ks, kw, False,
-                                                         with_copy=False))
+                                                         with_copy=False, warm_min_s=0.3))
         ov = run_overlap(args, synth.OVERLAP, min(args.steps, 8), min(args.warmup, 2))
         others[synth.OVERLAP.name] = {
             "tokens_per_s": ov["value"], "steps": ov["steps"], **ov["overlap"],
