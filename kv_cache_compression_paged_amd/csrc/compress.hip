@@ -1,5 +1,5 @@
-// Compression kernel: one workgroup of 8 waves per (request, layer, KV head)
-// unit scores, selects and compacts that unit.
+// Compression kernel: one workgroup per (request, layer, KV head) unit
+// scores, selects and compacts that unit.
 //
 // Steps, in the order of the method ([zh] §2.1, [de] §2, [es] §2):
 //   phase 1  sweep the unit's keys once through the block table: window
@@ -23,13 +23,19 @@
 // one CU streams its unit's rows other CUs are in their MFMA/exp sweeps: the
 // copy traffic overlaps the scoring work instead of following it.
 //
-// Organisation (gfx950). Wave w is (key quarter kq = w % 4, row half
-// rg = w / 4): at step s the two waves of quarter kq handle key block
-// 4s + kq, each for its half of the window rows, whose MFMA A fragments
-// stay in registers for the whole unit. Key blocks reach LDS by direct
-// global->LDS loads (16 bytes per lane, 1 KiB fully coalesced per
-// instruction) into a ring of NS slots per quarter (NS = 7 for bf16 with
-// head_dim 128, so up to five blocks per quarter are in flight without
+// Organisation (gfx950). A workgroup has KG key groups of two waves: wave w
+// is (key group kq = w % KG, row half rg = w / KG); at step s the two waves
+// of group kq handle key block KG*s + kq, each for its half of the window
+// rows, whose MFMA A fragments stay in registers for the whole unit. KG = 4
+// (8 waves, one workgroup per CU) takes units with more than 512 KiB of
+// keys; KG = 2 (4 waves, half the ring) puts two units on a CU, so one
+// unit's latency-bound phases (set-up, select) and its compaction overlap
+// the other's sweeps. Larger units stay at one per CU because the column
+// sweep's re-reads of a unit's keys are largely served by the last-level
+// cache, which holds one such unit per CU but not two. Key blocks reach LDS
+// by direct global->LDS loads (16 bytes per lane, 1 KiB fully coalesced per
+// instruction) into a ring of NS slots per key group (NS = 7 for bf16 with
+// head_dim 128, so up to five blocks per group are in flight without
 // costing registers); each wave of the pair issues half of a block's loads.
 // The 16-byte chunks of a block row are XOR-swizzled by row in LDS, so the
 // ds_read_b128 fragment reads (lane (j, n) takes row n, chunk group j) hit
@@ -37,7 +43,7 @@
 // wave's own loads plus a raw s_barrier (a __syncthreads would drain every
 // load in flight). Two waves share a SIMD, so one's MFMA overlaps the
 // other's exp/VALU work. Long contexts (token rows that do not fit beside
-// the default ring in LDS) take a 4-slot ring. The column sweep runs
+// the default 8-wave ring in LDS) take a 4-slot ring. The column sweep runs
 // backward: it starts on the blocks the first sweep read last and takes the
 // ones still in the ring without reloading them. In the column sweep the
 // two waves of a SIMD meet the barrier together, so for two unmasked blocks
@@ -632,14 +638,30 @@ void compress_kernel(ScoreArgs a) {
     }
   });
   __syncthreads();  // the attention row is complete (same workgroup, via L2)
-  for (int t = tid; t < n; t += kThreads) {
-    const float at = a.attn[urow + t];
-    const float rd = s_tok[t];
-    float sc = fmaf(a.w_attn, at, fmaf(a.w_global, grow[t], -a.w_red * rd));
-    if (t < pin_lo || t >= pin_hi) sc = INFINITY;
-    if (a.red) a.red[urow + t] = rd;
-    if (a.score) a.score[urow + t] = sc;
-    s_tok[t] = __uint_as_float(zpd::order_key(sc));
+  // In chunks of 8 tokens per thread, every load of a chunk is issued before
+  // any of its stores (the optional red/score stores would otherwise keep
+  // each iteration's loads behind the previous one's stores).
+  constexpr int kComb = 8;
+  for (int c0 = 0; c0 < n; c0 += kComb * kThreads) {
+    float at[kComb], gt[kComb];
+#pragma unroll
+    for (int j = 0; j < kComb; ++j) {
+      const int t = c0 + j * kThreads + tid;
+      at[j] = t < n ? a.attn[urow + t] : 0.f;
+      gt[j] = t < n ? grow[t] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < kComb; ++j) {
+      const int t = c0 + j * kThreads + tid;
+      if (t < n) {
+        const float rd = s_tok[t];
+        float sc = fmaf(a.w_attn, at[j], fmaf(a.w_global, gt[j], -a.w_red * rd));
+        if (t < pin_lo || t >= pin_hi) sc = INFINITY;
+        if (a.red) a.red[urow + t] = rd;
+        if (a.score) a.score[urow + t] = sc;
+        s_tok[t] = __uint_as_float(zpd::order_key(sc));
+      }
+    }
   }
   __syncthreads();
 
@@ -754,7 +776,7 @@ void compress_kernel(ScoreArgs a) {
   // before any of them is written, and a later chunk reads only at or above
   // its own start (keep[t] >= t), never what an earlier chunk wrote.
   if (a.flags & ZP_UPDATE_GLOBAL) {
-    constexpr int kPer = 4;
+    constexpr int kPer = 8;  // one chunk covers 4096 (8 waves) or 2048 tokens
     for (int c0 = 0; c0 < a.n_cap; c0 += kPer * kThreads) {
       float gv[kPer];
 #pragma unroll
