@@ -215,7 +215,12 @@ zp_status zp_compress_workspace_bytes(const zp_kv_pool* pool,
  * zp_update_global). workspace: device, 256-byte aligned, at least
  * zp_compress_workspace_bytes; it also receives the device error word.
  * Schedules. By default one workgroup scores, selects and compacts a whole
- * unit. With ZP_SPLIT_UNITS, a bf16 call with n_cap <= 4096 (w*G <= 128) or
+ * unit: units whose keys take at most 512 KiB (n_cap * head_dim * element
+ * bytes) run as 4-wave workgroups, two per compute unit, larger ones as
+ * 8-wave workgroups, one per compute unit. The environment variable
+ * ZIPAGE_KEY_GROUPS, read at each call, forces the 4-wave (value 2) or the
+ * 8-wave shape (value 4); both give results within the attention rounding
+ * of each other. With ZP_SPLIT_UNITS, a bf16 call with n_cap <= 4096 (w*G <= 128) or
  * n_cap <= 2048 (w*G <= 192) and a workspace of zp_compress_workspace_bytes
  * splits every unit over up to 8 workgroups, one per slice of 512 (256)
  * tokens: each keeps its slice's keys on chip, the workgroups exchange their
