@@ -478,6 +478,14 @@ def run_decode(args):
     }), flush=True)
 
 
+def all_pairs_flops(units: int, n: int, d: int, b: int = 16) -> float:
+    """MFMA work of the all-pairs cosine matrix as the kernel forms it: every
+    pair of b-row key tiles once (the matrix is symmetric), nt (nt + 1) / 2
+    tile products of 2 b^2 d flops per unit, nt = ceil(n / b)."""
+    nt = (n + b - 1) // b
+    return units * (nt * (nt + 1) / 2) * 2.0 * b * b * d
+
+
 def run_redundancy_ablation(args):
     """All-pairs redundancy (the score lightning replaces) against the whole
     compression step on the same units: 4 requests x 32 layers x 8 KV heads of
@@ -522,7 +530,7 @@ def run_redundancy_ablation(args):
                                          out, ws), "compress")
     if Z.zp_workspace_error(ws) != Z.ZP_OK:
         raise RuntimeError("device error in the ablation run")
-    flops_full = U * 2.0 * n * n * d
+    flops_full = all_pairs_flops(U, n, d)
     print(json.dumps({
         "metric": "all-pairs redundancy vs lightning (whole compression step), same units",
         "value": round(t_full / t_comp, 2), "unit": "x slower than the full compression",
@@ -592,7 +600,7 @@ def run_redundancy_sweep(args):
                                              params, out, ws), "compress")
         if Z.zp_workspace_error(ws) != Z.ZP_OK:
             raise RuntimeError("device error in the sweep")
-        flops = U * 2.0 * n * n * d
+        flops = all_pairs_flops(U, n, d)
         rows.append({"n_max": n_max, "tokens": n, "all_pairs_ms": round(t_all, 4),
                      "compress_ms": round(t_comp, 4),
                      "all_pairs_TFLOPs": round(flops / (t_all * 1e-3) / 1e12, 1),

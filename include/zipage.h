@@ -337,8 +337,12 @@ zp_status zp_paged_decode_split_static(float* out, const void* q, const void* k_
  * to zp_compress's red, up to rounding), and, when red_all is not NULL,
  * red_all[u][t], the mean over all other tokens. Rows [0, n) of
  * [U][n_cap] fp32 outputs are written; only src_table and n_tokens of the
- * batch are read. Nothing is moved or selected. workspace: as zp_compress
- * (its error word; a bad table entry gives ZP_EDEVICE there).
+ * batch are read. Nothing is moved or selected. Each pair of key tiles is
+ * formed once; red_all's sums gather contributions from several workgroups
+ * by float atomic adds, so they can differ between calls in the last bits
+ * (fp32 addition order). Without red_all only the block-diagonal tiles are
+ * formed. workspace: as zp_compress (its error word; a bad table entry gives
+ * ZP_EDEVICE there, and that unit's red_all rows are left at 0).
  * Errors: as zp_compress. */
 zp_status zp_redundancy_full(float* red_block, float* red_all, const zp_kv_pool* pool,
                              const zp_batch* batch, const zp_params* params,

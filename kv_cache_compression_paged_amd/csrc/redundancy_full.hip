@@ -6,11 +6,21 @@
 // The unit's n x n key Gram matrix is a dense contraction over head_dim, so
 // it runs as a tiled product on MFMA. A workgroup of 4 waves owns a panel of
 // row tiles (4 per wave for 16-byte-per-lane-chunk fragments, 2 for fp32
-// with head_dim 128); their fragments stay in registers while the unit's
-// column tiles stream past, four per step, through a 3-slot LDS ring filled
-// by direct global->LDS loads (each wave loads one tile; rows are
-// XOR-swizzled so the fragment reads hit distinct banks). One step costs
-// each wave 4 x RT tile products against one LDS read of each column tile.
+// with head_dim 128); their fragments stay in registers while column tiles
+// stream past, four per step, through a 3-slot LDS ring filled by direct
+// global->LDS loads (each wave loads one tile; rows are XOR-swizzled so the
+// fragment reads hit distinct banks). One step costs each wave up to
+// 4 x RT tile products against one LDS read of each column tile.
+//
+// The cosine matrix is symmetric, so every pair of tiles is formed once: a
+// panel takes the column tiles from its own first tile on and skips the
+// products below the diagonal. An off-diagonal product (row tile i, column
+// tile j > i) adds its row sums to tile i's tokens and its column sums to
+// tile j's, which belong to another wave or panel: all-token sums therefore
+// go to red_all by float atomic adds (zeroed before, divided by n - 1 after,
+// by two small kernels), so red_all is exact up to the order of fp32
+// additions. Diagonal tiles give their rows both sums and the same-block
+// sums, which their owner writes directly.
 //
 // Cosines: cos(i, j) = g_ij / max(|k_i| |k_j|, 1e-8). Wherever every pair of
 // a (row tiles, column tile) step clears the clamp -- the wave's smallest
@@ -62,6 +72,8 @@ struct Geo {
   static constexpr int kSwz = kRowChunks < 16 ? kRowChunks - 1 : 15;
   static constexpr int RT = Frag<E, D>::kChunks <= 4 ? 4 : 2;  // row tiles per wave
   static constexpr int kPanelTiles = kWaves * RT;
+  // two workgroups per CU, except fp32 with head_dim 128 (its ring fills LDS)
+  static constexpr int kWavesPerSimd = kTileBytes > 4096 ? 1 : 2;
   __device__ static constexpr int chunk_off(int row, int c) {
     return row * kRowBytes + ((c ^ (row & kSwz)) << 4);
   }
@@ -92,13 +104,17 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 template <typename E, int D>
-__global__ __launch_bounds__(kThreads) void redundancy_full_kernel(FullArgs a) {
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(Geo<E, D>::kWavesPerSimd)))
+void redundancy_full_kernel(FullArgs a) {
   using FragT = Frag<E, D>;
   using GE = Geo<E, D>;
   constexpr int RT = GE::RT;
   __shared__ __attribute__((aligned(16))) char ring[kRing][kWaves][GE::kTileBytes];
   __shared__ float cn2[2][kWaves][kB];   // squared norms of the step's columns
   __shared__ float cmin[2][kWaves];      // smallest valid one per tile
+  __shared__ float colw[2][kWaves][4][kB];  // each wave's column sums of a step's tiles
+  __shared__ float rnorm2[kWaves][RT][kB];  // squared norms of each wave's rows
   __shared__ int tab[1024];
 
   const int tid = threadIdx.x;
@@ -122,6 +138,10 @@ __global__ __launch_bounds__(kThreads) void redundancy_full_kernel(FullArgs a) {
   }
   const int tile0 = panel * GE::kPanelTiles;
   if (tile0 >= nt) return;
+  // with red_all the panel's rows meet every column tile from its own first
+  // tile on; without, only the diagonal tiles are needed
+  const bool all_pairs = a.red_all != nullptr;
+  const int ct_end = all_pairs ? nt : min(nt, tile0 + GE::kPanelTiles);
   const int32_t* src_tab = a.src_table + static_cast<int64_t>(r) * a.max_blocks;
   bool bad = false;
   for (int j = tid; j < nt; j += kThreads) {
@@ -139,7 +159,7 @@ __global__ __launch_bounds__(kThreads) void redundancy_full_kernel(FullArgs a) {
 
   // ---- this wave's row tiles: fragments and squared row norms
   FragT A[RT];
-  float rn2[RT][4];
+  float rinv[RT][4];
   float rmin2 = INFINITY;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -154,8 +174,12 @@ __global__ __launch_bounds__(kThreads) void redundancy_full_kernel(FullArgs a) {
     own += zpd::shfl_xor(own, 16);
     own += zpd::shfl_xor(own, 32);
     if (grt < nt && row < n) rmin2 = fminf(rmin2, own);
+    if (jg == 0) rnorm2[wave][rt][nl] = own;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) rn2[rt][i] = __shfl(own, 4 * jg + i, 64);
+    for (int i = 0; i < 4; ++i) {
+      const float r2 = __shfl(own, 4 * jg + i, 64);
+      rinv[rt][i] = r2 > 0.f ? __builtin_amdgcn_rsqf(r2) : 0.f;
+    }
   }
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) rmin2 = fminf(rmin2, zpd::shfl_xor(rmin2, o));
@@ -173,8 +197,8 @@ __global__ __launch_bounds__(kThreads) void redundancy_full_kernel(FullArgs a) {
   for (int c = 0; c < FragT::kChunks; ++c)
     frag_off[c] = GE::chunk_off(nl, jg * FragT::kChunks + c);
   auto issue = [&](int s) {  // this wave's column tile of step s
-    const int ct = 4 * s + wave;
-    if (ct >= nt) return;
+    const int ct = tile0 + 4 * s + wave;
+    if (ct >= ct_end) return;
     const char* src = base + tab[ct] * block_stride;
     char* dst = ring[s % kRing][wave];
 #pragma unroll
@@ -195,19 +219,31 @@ __global__ __launch_bounds__(kThreads) void redundancy_full_kernel(FullArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) fact[rt][i] = exact[rt][i] = blk[rt][i] = 0.f;
 
-  const int nsteps = (nt + 3) / 4;
+  const int64_t urow = static_cast<int64_t>(u) * a.n_cap;
+  // column sums of step s, after the barrier that follows it: wave w adds
+  // the four waves' sums for column tile w of that step to red_all
+  auto flush = [&](int s) {
+    const int ct = tile0 + 4 * s + wave;
+    const int col = ct * kB + lane;
+    if (!all_pairs || ct >= ct_end || lane >= kB || col >= n) return;
+    const float v = (colw[s & 1][0][wave][lane] + colw[s & 1][1][wave][lane]) +
+                    (colw[s & 1][2][wave][lane] + colw[s & 1][3][wave][lane]);
+    unsafeAtomicAdd(&a.red_all[urow + col], v);
+  };
+  const int nsteps = (ct_end - tile0 + 3) / 4;
   issue(0);
   for (int s = 0; s < nsteps; ++s) {
     // the slot step s+1 fills was last read in step s-2, which every wave
     // finished before the barriers of step s-1
-    const bool more = s + 1 < nsteps && 4 * (s + 1) + wave < nt;
+    const bool more = s + 1 < nsteps && tile0 + 4 * (s + 1) + wave < ct_end;
     if (s + 1 < nsteps) issue(s + 1);
     wait_vm_lgkm0(more ? GE::kLoads : 0);
     raw_barrier();  // step s's tiles have landed (every wave waited on its own)
+    if (s > 0) flush(s - 1);  // step s-1's column sums are complete
     const int slot = s % kRing;
     {
-      const int ct = 4 * s + wave;
-      if (ct < nt) {
+      const int ct = tile0 + 4 * s + wave;
+      if (ct < ct_end) {
         FragT f;
         read_frag(f, slot, wave);
         const bool ok = ct * kB + nl < n;
@@ -224,8 +260,8 @@ __global__ __launch_bounds__(kThreads) void redundancy_full_kernel(FullArgs a) {
     lds_barrier();
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const int ct = 4 * s + c;
-      if (ct >= nt) break;
+      const int ct = tile0 + 4 * s + c;
+      if (ct >= ct_end) break;
       const int col = ct * kB + nl;
       const bool ok = col < n;
       FragT f;
@@ -234,47 +270,80 @@ __global__ __launch_bounds__(kThreads) void redundancy_full_kernel(FullArgs a) {
       const float c2 = cn2[s & 1][c][nl];
       const bool safe = rmin2 * cmin[s & 1][c] >= 1e-16f;
       const float cinv = (ok && safe) ? __builtin_amdgcn_rsqf(c2) : 0.f;
-      f32x4_t g[RT];
-      if constexpr (E::kBytes == 2) {
-        // chunk-major: the RT accumulation chains interleave
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) g[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int k = 0; k < FragT::kChunks; ++k)
-#pragma unroll
-          for (int rt = 0; rt < RT; ++rt)
-            g[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(zpd::bf16x8_t, A[rt].v[k]),
-                __builtin_bit_cast(zpd::bf16x8_t, f.v[k]), g[rt], 0, 0, 0);
-      } else {
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-          g[rt] = zpd::mma_rows<E, D>(A[rt], f, f32x4_t{0.f, 0.f, 0.f, 0.f});
-      }
+      // which of this wave's row tiles pair with column tile ct: those at or
+      // below it (at it only, without red_all); the others were or will be
+      // formed as (ct, row tile) by the owner of ct
+      bool use[RT];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         const int grt = tile0 + wave * RT + rt;
-        if (grt >= nt) continue;
+        use[rt] = grt < nt && (all_pairs ? grt <= ct : grt == ct);
+      }
+      f32x4_t g[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) g[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      // past the wave's last row tile every row tile pairs with ct (rows
+      // beyond n are zero fragments): the products run unguarded
+      const bool every = all_pairs && ct >= tile0 + wave * RT + RT - 1;
+      if constexpr (E::kBytes == 2) {
+        // chunk-major: the RT accumulation chains interleave
+        if (every) {
+#pragma unroll
+          for (int k = 0; k < FragT::kChunks; ++k)
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+              g[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(zpd::bf16x8_t, A[rt].v[k]),
+                  __builtin_bit_cast(zpd::bf16x8_t, f.v[k]), g[rt], 0, 0, 0);
+        } else {
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+            if (use[rt]) g[rt] = zpd::mma_rows<E, D>(A[rt], f, f32x4_t{0.f, 0.f, 0.f, 0.f});
+        }
+      } else {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+          if (every || use[rt]) g[rt] = zpd::mma_rows<E, D>(A[rt], f, f32x4_t{0.f, 0.f, 0.f, 0.f});
+      }
+      float colf = 0.f, colx = 0.f;  // this lane's share of column nl's sums
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        if (!use[rt]) continue;
+        const int grt = tile0 + wave * RT + rt;
         if (ct != grt && safe) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) fact[rt][i] = fmaf(g[rt][i], cinv, fact[rt][i]);
+          for (int i = 0; i < 4; ++i) {
+            fact[rt][i] = fmaf(g[rt][i], cinv, fact[rt][i]);
+            colf = fmaf(g[rt][i], rinv[rt][i], colf);
+          }
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int row = grt * kB + 4 * jg + i;
+            const float r2 = rnorm2[wave][rt][4 * jg + i];
             const float cv = (ok && row != col)
-                                 ? g[rt][i] * __builtin_amdgcn_rsqf(fmaxf(rn2[rt][i] * c2, 1e-16f))
+                                 ? g[rt][i] * __builtin_amdgcn_rsqf(fmaxf(r2 * c2, 1e-16f))
                                  : 0.f;
             exact[rt][i] += cv;
             if (ct == grt) blk[rt][i] += cv;
+            else colx += cv;
           }
         }
       }
+      if (all_pairs) {
+        // the 16 rows of a column sit in the four lane groups
+        float cs = fmaf(colf, cinv, colx);
+        cs += zpd::shfl_xor(cs, 16);
+        cs += zpd::shfl_xor(cs, 32);
+        if (jg == 0) colw[s & 1][wave][c][nl] = cs;
+      }
     }
   }
+  lds_barrier();  // the last step's column sums are complete
+  if (nsteps > 0) flush(nsteps - 1);
 
-  // ---- row sums over the 16 columns a lane group holds, then the means
-  const int64_t urow = static_cast<int64_t>(u) * a.n_cap;
+  // ---- row sums over the 16 columns a lane group holds: the same-block
+  // mean directly, the all-token sum added to red_all
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int grt = tile0 + wave * RT + rt;
@@ -288,14 +357,24 @@ __global__ __launch_bounds__(kThreads) void redundancy_full_kernel(FullArgs a) {
       }
       const int row = grt * kB + 4 * jg + i;
       if (nl == 0 && grt < nt && row < n) {
-        const float rinv = rn2[rt][i] > 0.f ? __builtin_amdgcn_rsqf(rn2[rt][i]) : 0.f;
-        const float all = fmaf(fact[rt][i], rinv, exact[rt][i]);
         const int cnt = min(kB, n - grt * kB);
         a.red_block[urow + row] = cnt >= 2 ? blk[rt][i] / (cnt - 1) : 0.f;
-        if (a.red_all) a.red_all[urow + row] = n >= 2 ? all / (n - 1) : 0.f;
+        if (all_pairs)
+          unsafeAtomicAdd(&a.red_all[urow + row], fmaf(fact[rt][i], rinv[rt][i], exact[rt][i]));
       }
     }
   }
+}
+
+// rows [0, n) of a unit's red_all: zeroed before the atomic sums, then
+// divided by n - 1 (0 for n < 2); one workgroup per unit
+__global__ __launch_bounds__(kThreads) void full_rows_kernel(FullArgs a, int finish) {
+  const int u = blockIdx.x;
+  const int r = u / (a.Hkv * a.L);
+  const int n = min(max(a.n_tokens[r], 0), a.n_cap);
+  float* row = a.red_all + static_cast<int64_t>(u) * a.n_cap;
+  const float inv = n >= 2 ? 1.f / static_cast<float>(n - 1) : 0.f;
+  for (int t = threadIdx.x; t < n; t += kThreads) row[t] = finish ? row[t] * inv : 0.f;
 }
 
 template <typename E, int D>
@@ -306,8 +385,13 @@ zp_status launch_full(FullArgs a, void* stream) {
   if (grid > (1ll << 31) - 1)
     return zp::fail(ZP_EINVAL, "all-pairs redundancy: %lld workgroups",
                     static_cast<long long>(grid));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (a.red_all)
+    hipLaunchKernelGGL(full_rows_kernel, dim3(a.units), dim3(kThreads), 0, st, a, 0);
   hipLaunchKernelGGL((redundancy_full_kernel<E, D>), dim3(static_cast<unsigned>(grid)),
-                     dim3(kThreads), 0, static_cast<hipStream_t>(stream), a);
+                     dim3(kThreads), 0, st, a);
+  if (a.red_all)
+    hipLaunchKernelGGL(full_rows_kernel, dim3(a.units), dim3(kThreads), 0, st, a, 1);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess)
     return zp::fail(ZP_EHIP, "all-pairs redundancy launch: %s", hipGetErrorString(e));

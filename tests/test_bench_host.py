@@ -5,7 +5,8 @@
 * bench.py reports a summary's traffic only while the hash of the kernel's
   sources matches the one recorded with the counters (a changed kernel gets
   null, not stale numbers);
-* more than one GPU is refused with a message.
+* more than one GPU is refused with a message;
+* the all-pairs ablation counts each pair of key tiles once.
 """
 
 import glob
@@ -69,3 +70,14 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_all_pairs_work_counts_each_tile_pair_once():
+    # nt tiles give nt (nt + 1) / 2 tile pairs (the diagonal included), each
+    # 2 b^2 d flops; for full tiles that is (n^2 + n b) d, about half the
+    # 2 n^2 d of the whole Gram matrix
+    assert bench.all_pairs_flops(1, 16, 128) == 2 * 16 * 16 * 128
+    assert bench.all_pairs_flops(1, 32, 64) == 3 * 2 * 16 * 16 * 64
+    assert bench.all_pairs_flops(1, 33, 64) == 6 * 2 * 16 * 16 * 64   # ragged: 3 tiles
+    n, d = 4096, 128
+    assert bench.all_pairs_flops(5, n, d) == 5 * (n * n + n * 16) * d
