@@ -402,7 +402,7 @@ void compress_kernel(ScoreArgs a) {
       mr[rt][i] = -INFINITY;
     }
   sweep([&](const FragT& kc, int s, Acc& acc) { logits(kc, acc, (s & 1) == rg); },
-        [&](const Acc& acc, int kt, int s) {
+        [&](Acc& acc, int kt, int s) {  // masked entries of acc become -inf
     const int t = kt * kB + nl;
     if (s == 0) {  // first block of this wave: the references
 #pragma unroll
@@ -415,20 +415,27 @@ void compress_kernel(ScoreArgs a) {
           mr[rt][i] = v;
         }
     }
-    if (!tile_masked(kt)) {
+    // One accumulation path for every block: in a masked block the entries
+    // outside the mask become -inf first (exp2 gives 0). (Two paths made the
+    // compiler copy every accumulator back after each unmasked block.) A row
+    // whose reference is -inf gets NaN or inf either way and takes the exact
+    // pass below.
+    if (tile_masked(kt)) {
 #pragma unroll
       for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          z[rt][i] += zpd::fast_exp2(fmaf(acc.a[rt][i], sl2, -mr[rt][i]));
-    } else {
-#pragma unroll
-      for (int rt = 0; rt < RTW; ++rt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (entry_ok(rt, i, t))
-            z[rt][i] += zpd::fast_exp2(fmaf(acc.a[rt][i], sl2, -mr[rt][i]));
+          if (!entry_ok(rt, i, t)) acc.a[rt][i] = -INFINITY;
     }
+    // all exponentials first (independent), then the sums
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc.a[rt][i] = zpd::fast_exp2(fmaf(acc.a[rt][i], sl2, -mr[rt][i]));
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) z[rt][i] += acc.a[rt][i];
     // lightning redundancy of block kt (the pair alternates by step):
     // column sums of the block's cosine matrix
     if ((s & 1) == rg) {
@@ -827,25 +834,51 @@ void compress_kernel(ScoreArgs a) {
   struct Buf {
     zpd::u32x4_t vk[kPasses], vv[kPasses];
   };
-  // rows past k are clamped to row k-1 (always valid) and not stored
+  // rows past k are clamped to row k-1 (always valid) and not stored.
+  // Row offsets: a block id (checked, non-negative) times the block stride
+  // (Hkv tiles, below 2^32 bytes) in one 32 x 32 -> 64-bit multiply-add; a
+  // chunk's LDS lookups are issued together (all positions, then all block
+  // ids), so it waits on LDS twice rather than once per row.
+  const uint32_t bstride = static_cast<uint32_t>(block_stride);
+  auto row_off = [&](int blk, uint32_t slot) {
+    return static_cast<uint64_t>(static_cast<uint32_t>(blk)) * bstride +
+           (slot * TG::kRowBytes + static_cast<uint32_t>(piece16));
+  };
   auto load_chunk = [&](int c0, Buf& bf) {
+    int sp[kPasses], blk[kPasses];
+#pragma unroll
+    for (int e = 0; e < kPasses; ++e) sp[e] = keep_l[min(c0 + e * kRowsPerPass + prow, k - 1)];
+#pragma unroll
+    for (int e = 0; e < kPasses; ++e) blk[e] = tab[static_cast<uint32_t>(sp[e]) / kB];
 #pragma unroll
     for (int e = 0; e < kPasses; ++e) {
-      const int t = min(c0 + e * kRowsPerPass + prow, k - 1);
-      const int sp = keep_l[t];
-      const int64_t soff = tab[sp / kB] * block_stride + (sp % kB) * TG::kRowBytes + piece16;
+      const uint64_t soff = row_off(blk[e], static_cast<uint32_t>(sp[e]) % kB);
       bf.vk[e] = __builtin_nontemporal_load(reinterpret_cast<const zpd::u32x4_t*>(kmut + soff));
       bf.vv[e] = __builtin_nontemporal_load(reinterpret_cast<const zpd::u32x4_t*>(vmut + soff));
     }
   };
   auto store_chunk = [&](int c0, const Buf& bf) {
+    int blk[kPasses];
 #pragma unroll
-    for (int e = 0; e < kPasses; ++e) {
-      const int t = c0 + e * kRowsPerPass + prow;
-      if (t < k) {
-        const int64_t doff = dtab[t / kB] * block_stride + (t % kB) * TG::kRowBytes + piece16;
+    for (int e = 0; e < kPasses; ++e)
+      blk[e] = dtab[static_cast<uint32_t>(min(c0 + e * kRowsPerPass + prow, k - 1)) / kB];
+    if (c0 + kRowsPerChunk <= k) {  // every row of the chunk is stored
+#pragma unroll
+      for (int e = 0; e < kPasses; ++e) {
+        const uint32_t t = static_cast<uint32_t>(c0 + e * kRowsPerPass + prow);
+        const uint64_t doff = row_off(blk[e], t % kB);
         __builtin_nontemporal_store(bf.vk[e], reinterpret_cast<zpd::u32x4_t*>(kmut + doff));
         __builtin_nontemporal_store(bf.vv[e], reinterpret_cast<zpd::u32x4_t*>(vmut + doff));
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < kPasses; ++e) {
+        const int t = c0 + e * kRowsPerPass + prow;
+        if (t < k) {
+          const uint64_t doff = row_off(blk[e], static_cast<uint32_t>(t) % kB);
+          __builtin_nontemporal_store(bf.vk[e], reinterpret_cast<zpd::u32x4_t*>(kmut + doff));
+          __builtin_nontemporal_store(bf.vv[e], reinterpret_cast<zpd::u32x4_t*>(vmut + doff));
+        }
       }
     }
   };
