@@ -125,23 +125,22 @@ void redundancy_full_kernel(FullArgs a) {
   // id (b % 8) * (grid / 8) + b / 8, so consecutive ids share an XCD
   const int per_xcd = gridDim.x / kXcds;
   const int lid = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-  if (lid >= a.units * a.panels) return;
-  const int u = lid / a.panels, panel = lid - u * a.panels;
+  // a workgroup takes panels pp and P - 1 - pp, a long and a short row of
+  // the triangle of tile pairs, so every workgroup has about the same work
+  const int pairs = (a.panels + 1) / 2;
+  if (lid >= a.units * pairs) return;
+  const int u = lid / pairs, pp = lid - u * pairs;
   const int h = u % a.Hkv;
   const int l = (u / a.Hkv) % a.L;
   const int r = u / (a.Hkv * a.L);
   const int n = a.n_tokens[r];
   const int nt = (n + kB - 1) / kB;
   if (n < 1 || n > a.n_cap || nt > a.max_blocks || nt > 1024) {
-    if (tid == 0 && panel == 0) *a.err = ZP_EDEVICE;
+    if (tid == 0 && pp == 0) *a.err = ZP_EDEVICE;
     return;
   }
-  const int tile0 = panel * GE::kPanelTiles;
-  if (tile0 >= nt) return;
-  // with red_all the panel's rows meet every column tile from its own first
-  // tile on; without, only the diagonal tiles are needed
+  if (pp * GE::kPanelTiles >= nt) return;  // both panels lie beyond n
   const bool all_pairs = a.red_all != nullptr;
-  const int ct_end = all_pairs ? nt : min(nt, tile0 + GE::kPanelTiles);
   const int32_t* src_tab = a.src_table + static_cast<int64_t>(r) * a.max_blocks;
   bool bad = false;
   for (int j = tid; j < nt; j += kThreads) {
@@ -156,214 +155,228 @@ void redundancy_full_kernel(FullArgs a) {
   const char* base = static_cast<const char*>(a.kpool) +
                      (static_cast<int64_t>(l) * a.NB * a.Hkv + h) * GE::kTileBytes;
   const int64_t block_stride = static_cast<int64_t>(a.Hkv) * GE::kTileBytes;
-
-  // ---- this wave's row tiles: fragments and squared row norms
-  FragT A[RT];
-  float rinv[RT][4];
-  float rmin2 = INFINITY;
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int grt = tile0 + wave * RT + rt;
-    const int row = grt * kB + nl;
-    if (grt < nt && row < n)
-      A[rt].load(base + tab[grt] * block_stride + nl * GE::kRowBytes +
-                 jg * (D / 4) * E::kBytes);
-    else
-      A[rt].zero();
-    float own = A[rt].sumsq();
-    own += zpd::shfl_xor(own, 16);
-    own += zpd::shfl_xor(own, 32);
-    if (grt < nt && row < n) rmin2 = fminf(rmin2, own);
-    if (jg == 0) rnorm2[wave][rt][nl] = own;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float r2 = __shfl(own, 4 * jg + i, 64);
-      rinv[rt][i] = r2 > 0.f ? __builtin_amdgcn_rsqf(r2) : 0.f;
-    }
-  }
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) rmin2 = fminf(rmin2, zpd::shfl_xor(rmin2, o));
-
-  // ---- column sweep: step s covers column tiles 4s .. 4s+3
-  int src_off[GE::kLoads];
-#pragma unroll
-  for (int e = 0; e < GE::kLoads; ++e) {
-    const int sidx = e * 64 + lane;
-    const int row = sidx / GE::kRowChunks, pos = sidx % GE::kRowChunks;
-    src_off[e] = row * GE::kRowBytes + ((pos ^ (row & GE::kSwz)) << 4);
-  }
-  int frag_off[FragT::kChunks];
-#pragma unroll
-  for (int c = 0; c < FragT::kChunks; ++c)
-    frag_off[c] = GE::chunk_off(nl, jg * FragT::kChunks + c);
-  auto issue = [&](int s) {  // this wave's column tile of step s
-    const int ct = tile0 + 4 * s + wave;
-    if (ct >= ct_end) return;
-    const char* src = base + tab[ct] * block_stride;
-    char* dst = ring[s % kRing][wave];
-#pragma unroll
-    for (int e = 0; e < GE::kLoads; ++e)
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + src_off[e]),
-                                       (ZP_LDS void*)(dst + e * 1024), 16, 0, 0);
-  };
-  auto read_frag = [&](FragT& f, int slot, int c) {
-    const char* p = ring[slot][c];
-#pragma unroll
-    for (int k = 0; k < FragT::kChunks; ++k)
-      f.v[k] = *reinterpret_cast<const zpd::u32x4_t*>(p + frag_off[k]);
-  };
-
-  float fact[RT][4], exact[RT][4], blk[RT][4];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) fact[rt][i] = exact[rt][i] = blk[rt][i] = 0.f;
-
   const int64_t urow = static_cast<int64_t>(u) * a.n_cap;
-  // column sums of step s, after the barrier that follows it: wave w adds
-  // the four waves' sums for column tile w of that step to red_all
-  auto flush = [&](int s) {
-    const int ct = tile0 + 4 * s + wave;
-    const int col = ct * kB + lane;
-    if (!all_pairs || ct >= ct_end || lane >= kB || col >= n) return;
-    const float v = (colw[s & 1][0][wave][lane] + colw[s & 1][1][wave][lane]) +
-                    (colw[s & 1][2][wave][lane] + colw[s & 1][3][wave][lane]);
-    unsafeAtomicAdd(&a.red_all[urow + col], v);
-  };
-  const int nsteps = (ct_end - tile0 + 3) / 4;
-  issue(0);
-  for (int s = 0; s < nsteps; ++s) {
-    // the slot step s+1 fills was last read in step s-2, which every wave
-    // finished before the barriers of step s-1
-    const bool more = s + 1 < nsteps && tile0 + 4 * (s + 1) + wave < ct_end;
-    if (s + 1 < nsteps) issue(s + 1);
-    wait_vm_lgkm0(more ? GE::kLoads : 0);
-    raw_barrier();  // step s's tiles have landed (every wave waited on its own)
-    if (s > 0) flush(s - 1);  // step s-1's column sums are complete
-    const int slot = s % kRing;
-    {
-      const int ct = tile0 + 4 * s + wave;
-      if (ct < ct_end) {
-        FragT f;
-        read_frag(f, slot, wave);
-        const bool ok = ct * kB + nl < n;
-        float sq = ok ? f.sumsq() : 0.f;
-        sq += zpd::shfl_xor(sq, 16);
-        sq += zpd::shfl_xor(sq, 32);
-        float mn = ok ? sq : INFINITY;
+
+  // One panel: its row tiles against column tiles from its own first tile on
+  // (with red_all; without, the diagonal tiles only). Two panels run one
+  // after the other: the second issues its first ring loads after every
+  // wave has passed the first's closing barrier (its last ring and
+  // column-sum reads precede it) and writes column sums only after its own
+  // first step's barrier.
+  auto run_panel = [&](const int panel) {
+    const int tile0 = panel * GE::kPanelTiles;
+    const int ct_end = all_pairs ? nt : min(nt, tile0 + GE::kPanelTiles);
+
+    // ---- this wave's row tiles: fragments and squared row norms
+    FragT A[RT];
+    float rinv[RT][4];
+    float rmin2 = INFINITY;
 #pragma unroll
-        for (int o = 1; o < 16; o <<= 1) mn = fminf(mn, zpd::shfl_xor(mn, o));
-        if (jg == 0) cn2[s & 1][wave][nl] = sq;
-        if (lane == 0) cmin[s & 1][wave] = mn;
+    for (int rt = 0; rt < RT; ++rt) {
+      const int grt = tile0 + wave * RT + rt;
+      const int row = grt * kB + nl;
+      if (grt < nt && row < n)
+        A[rt].load(base + tab[grt] * block_stride + nl * GE::kRowBytes +
+                   jg * (D / 4) * E::kBytes);
+      else
+        A[rt].zero();
+      float own = A[rt].sumsq();
+      own += zpd::shfl_xor(own, 16);
+      own += zpd::shfl_xor(own, 32);
+      if (grt < nt && row < n) rmin2 = fminf(rmin2, own);
+      if (jg == 0) rnorm2[wave][rt][nl] = own;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float r2 = __shfl(own, 4 * jg + i, 64);
+        rinv[rt][i] = r2 > 0.f ? __builtin_amdgcn_rsqf(r2) : 0.f;
       }
     }
-    lds_barrier();
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int ct = tile0 + 4 * s + c;
-      if (ct >= ct_end) break;
-      const int col = ct * kB + nl;
-      const bool ok = col < n;
-      FragT f;
-      read_frag(f, slot, c);
-      if (!ok) f.zero();
-      const float c2 = cn2[s & 1][c][nl];
-      const bool safe = rmin2 * cmin[s & 1][c] >= 1e-16f;
-      const float cinv = (ok && safe) ? __builtin_amdgcn_rsqf(c2) : 0.f;
-      // which of this wave's row tiles pair with column tile ct: those at or
-      // below it (at it only, without red_all); the others were or will be
-      // formed as (ct, row tile) by the owner of ct
-      bool use[RT];
+    for (int o = 1; o < 64; o <<= 1) rmin2 = fminf(rmin2, zpd::shfl_xor(rmin2, o));
+
+    // ---- column sweep: step s covers column tiles 4s .. 4s+3
+    int src_off[GE::kLoads];
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const int grt = tile0 + wave * RT + rt;
-        use[rt] = grt < nt && (all_pairs ? grt <= ct : grt == ct);
+    for (int e = 0; e < GE::kLoads; ++e) {
+      const int sidx = e * 64 + lane;
+      const int row = sidx / GE::kRowChunks, pos = sidx % GE::kRowChunks;
+      src_off[e] = row * GE::kRowBytes + ((pos ^ (row & GE::kSwz)) << 4);
+    }
+    int frag_off[FragT::kChunks];
+#pragma unroll
+    for (int c = 0; c < FragT::kChunks; ++c)
+      frag_off[c] = GE::chunk_off(nl, jg * FragT::kChunks + c);
+    auto issue = [&](int s) {  // this wave's column tile of step s
+      const int ct = tile0 + 4 * s + wave;
+      if (ct >= ct_end) return;
+      const char* src = base + tab[ct] * block_stride;
+      char* dst = ring[s % kRing][wave];
+#pragma unroll
+      for (int e = 0; e < GE::kLoads; ++e)
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + src_off[e]),
+                                         (ZP_LDS void*)(dst + e * 1024), 16, 0, 0);
+    };
+    auto read_frag = [&](FragT& f, int slot, int c) {
+      const char* p = ring[slot][c];
+#pragma unroll
+      for (int k = 0; k < FragT::kChunks; ++k)
+        f.v[k] = *reinterpret_cast<const zpd::u32x4_t*>(p + frag_off[k]);
+    };
+
+    float fact[RT][4], exact[RT][4], blk[RT][4];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fact[rt][i] = exact[rt][i] = blk[rt][i] = 0.f;
+
+    // column sums of step s, after the barrier that follows it: wave w adds
+    // the four waves' sums for column tile w of that step to red_all
+    auto flush = [&](int s) {
+      const int ct = tile0 + 4 * s + wave;
+      const int col = ct * kB + lane;
+      if (!all_pairs || ct >= ct_end || lane >= kB || col >= n) return;
+      const float v = (colw[s & 1][0][wave][lane] + colw[s & 1][1][wave][lane]) +
+                      (colw[s & 1][2][wave][lane] + colw[s & 1][3][wave][lane]);
+      unsafeAtomicAdd(&a.red_all[urow + col], v);
+    };
+    const int nsteps = (ct_end - tile0 + 3) / 4;
+    issue(0);
+    for (int s = 0; s < nsteps; ++s) {
+      // the slot step s+1 fills was last read in step s-2, which every wave
+      // finished before the barriers of step s-1
+      const bool more = s + 1 < nsteps && tile0 + 4 * (s + 1) + wave < ct_end;
+      if (s + 1 < nsteps) issue(s + 1);
+      wait_vm_lgkm0(more ? GE::kLoads : 0);
+      raw_barrier();  // step s's tiles have landed (every wave waited on its own)
+      if (s > 0) flush(s - 1);  // step s-1's column sums are complete
+      const int slot = s % kRing;
+      {
+        const int ct = tile0 + 4 * s + wave;
+        if (ct < ct_end) {
+          FragT f;
+          read_frag(f, slot, wave);
+          const bool ok = ct * kB + nl < n;
+          float sq = ok ? f.sumsq() : 0.f;
+          sq += zpd::shfl_xor(sq, 16);
+          sq += zpd::shfl_xor(sq, 32);
+          float mn = ok ? sq : INFINITY;
+#pragma unroll
+          for (int o = 1; o < 16; o <<= 1) mn = fminf(mn, zpd::shfl_xor(mn, o));
+          if (jg == 0) cn2[s & 1][wave][nl] = sq;
+          if (lane == 0) cmin[s & 1][wave] = mn;
+        }
       }
-      f32x4_t g[RT];
+      lds_barrier();
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) g[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      // past the wave's last row tile every row tile pairs with ct (rows
-      // beyond n are zero fragments): the products run unguarded
-      const bool every = all_pairs && ct >= tile0 + wave * RT + RT - 1;
-      if constexpr (E::kBytes == 2) {
-        // chunk-major: the RT accumulation chains interleave
-        if (every) {
+      for (int c = 0; c < 4; ++c) {
+        const int ct = tile0 + 4 * s + c;
+        if (ct >= ct_end) break;
+        const int col = ct * kB + nl;
+        const bool ok = col < n;
+        FragT f;
+        read_frag(f, slot, c);
+        if (!ok) f.zero();
+        const float c2 = cn2[s & 1][c][nl];
+        const bool safe = rmin2 * cmin[s & 1][c] >= 1e-16f;
+        const float cinv = (ok && safe) ? __builtin_amdgcn_rsqf(c2) : 0.f;
+        // which of this wave's row tiles pair with column tile ct: those at or
+        // below it (at it only, without red_all); the others were or will be
+        // formed as (ct, row tile) by the owner of ct
+        bool use[RT];
 #pragma unroll
-          for (int k = 0; k < FragT::kChunks; ++k)
+        for (int rt = 0; rt < RT; ++rt) {
+          const int grt = tile0 + wave * RT + rt;
+          use[rt] = grt < nt && (all_pairs ? grt <= ct : grt == ct);
+        }
+        f32x4_t g[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) g[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        // past the wave's last row tile every row tile pairs with ct (rows
+        // beyond n are zero fragments): the products run unguarded
+        const bool every = all_pairs && ct >= tile0 + wave * RT + RT - 1;
+        if constexpr (E::kBytes == 2) {
+          // chunk-major: the RT accumulation chains interleave
+          if (every) {
+#pragma unroll
+            for (int k = 0; k < FragT::kChunks; ++k)
+#pragma unroll
+              for (int rt = 0; rt < RT; ++rt)
+                g[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(zpd::bf16x8_t, A[rt].v[k]),
+                    __builtin_bit_cast(zpd::bf16x8_t, f.v[k]), g[rt], 0, 0, 0);
+          } else {
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
-              g[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  __builtin_bit_cast(zpd::bf16x8_t, A[rt].v[k]),
-                  __builtin_bit_cast(zpd::bf16x8_t, f.v[k]), g[rt], 0, 0, 0);
+              if (use[rt]) g[rt] = zpd::mma_rows<E, D>(A[rt], f, f32x4_t{0.f, 0.f, 0.f, 0.f});
+          }
         } else {
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt)
-            if (use[rt]) g[rt] = zpd::mma_rows<E, D>(A[rt], f, f32x4_t{0.f, 0.f, 0.f, 0.f});
+            if (every || use[rt]) g[rt] = zpd::mma_rows<E, D>(A[rt], f, f32x4_t{0.f, 0.f, 0.f, 0.f});
         }
-      } else {
+        float colf = 0.f, colx = 0.f;  // this lane's share of column nl's sums
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-          if (every || use[rt]) g[rt] = zpd::mma_rows<E, D>(A[rt], f, f32x4_t{0.f, 0.f, 0.f, 0.f});
-      }
-      float colf = 0.f, colx = 0.f;  // this lane's share of column nl's sums
+        for (int rt = 0; rt < RT; ++rt) {
+          if (!use[rt]) continue;
+          const int grt = tile0 + wave * RT + rt;
+          if (ct != grt && safe) {
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        if (!use[rt]) continue;
-        const int grt = tile0 + wave * RT + rt;
-        if (ct != grt && safe) {
+            for (int i = 0; i < 4; ++i) {
+              fact[rt][i] = fmaf(g[rt][i], cinv, fact[rt][i]);
+              colf = fmaf(g[rt][i], rinv[rt][i], colf);
+            }
+          } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            fact[rt][i] = fmaf(g[rt][i], cinv, fact[rt][i]);
-            colf = fmaf(g[rt][i], rinv[rt][i], colf);
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int row = grt * kB + 4 * jg + i;
-            const float r2 = rnorm2[wave][rt][4 * jg + i];
-            const float cv = (ok && row != col)
-                                 ? g[rt][i] * __builtin_amdgcn_rsqf(fmaxf(r2 * c2, 1e-16f))
-                                 : 0.f;
-            exact[rt][i] += cv;
-            if (ct == grt) blk[rt][i] += cv;
-            else colx += cv;
+            for (int i = 0; i < 4; ++i) {
+              const int row = grt * kB + 4 * jg + i;
+              const float r2 = rnorm2[wave][rt][4 * jg + i];
+              const float cv = (ok && row != col)
+                                   ? g[rt][i] * __builtin_amdgcn_rsqf(fmaxf(r2 * c2, 1e-16f))
+                                   : 0.f;
+              exact[rt][i] += cv;
+              if (ct == grt) blk[rt][i] += cv;
+              else colx += cv;
+            }
           }
         }
-      }
-      if (all_pairs) {
-        // the 16 rows of a column sit in the four lane groups
-        float cs = fmaf(colf, cinv, colx);
-        cs += zpd::shfl_xor(cs, 16);
-        cs += zpd::shfl_xor(cs, 32);
-        if (jg == 0) colw[s & 1][wave][c][nl] = cs;
+        if (all_pairs) {
+          // the 16 rows of a column sit in the four lane groups
+          float cs = fmaf(colf, cinv, colx);
+          cs += zpd::shfl_xor(cs, 16);
+          cs += zpd::shfl_xor(cs, 32);
+          if (jg == 0) colw[s & 1][wave][c][nl] = cs;
+        }
       }
     }
-  }
-  lds_barrier();  // the last step's column sums are complete
-  if (nsteps > 0) flush(nsteps - 1);
+    lds_barrier();  // the last step's column sums are complete
+    if (nsteps > 0) flush(nsteps - 1);
 
-  // ---- row sums over the 16 columns a lane group holds: the same-block
-  // mean directly, the all-token sum added to red_all
+    // ---- row sums over the 16 columns a lane group holds: the same-block
+    // mean directly, the all-token sum added to red_all
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int grt = tile0 + wave * RT + rt;
+    for (int rt = 0; rt < RT; ++rt) {
+      const int grt = tile0 + wave * RT + rt;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        fact[rt][i] += zpd::shfl_xor(fact[rt][i], o);
-        exact[rt][i] += zpd::shfl_xor(exact[rt][i], o);
-        blk[rt][i] += zpd::shfl_xor(blk[rt][i], o);
-      }
-      const int row = grt * kB + 4 * jg + i;
-      if (nl == 0 && grt < nt && row < n) {
-        const int cnt = min(kB, n - grt * kB);
-        a.red_block[urow + row] = cnt >= 2 ? blk[rt][i] / (cnt - 1) : 0.f;
-        if (all_pairs)
-          unsafeAtomicAdd(&a.red_all[urow + row], fmaf(fact[rt][i], rinv[rt][i], exact[rt][i]));
+        for (int o = 1; o < 16; o <<= 1) {
+          fact[rt][i] += zpd::shfl_xor(fact[rt][i], o);
+          exact[rt][i] += zpd::shfl_xor(exact[rt][i], o);
+          blk[rt][i] += zpd::shfl_xor(blk[rt][i], o);
+        }
+        const int row = grt * kB + 4 * jg + i;
+        if (nl == 0 && grt < nt && row < n) {
+          const int cnt = min(kB, n - grt * kB);
+          a.red_block[urow + row] = cnt >= 2 ? blk[rt][i] / (cnt - 1) : 0.f;
+          if (all_pairs)
+            unsafeAtomicAdd(&a.red_all[urow + row], fmaf(fact[rt][i], rinv[rt][i], exact[rt][i]));
+        }
       }
     }
-  }
+  };
+  run_panel(pp);
+  const int other = a.panels - 1 - pp;
+  if (other != pp && other * GE::kPanelTiles < nt) run_panel(other);
 }
 
 // rows [0, n) of a unit's red_all: zeroed before the atomic sums, then
@@ -380,7 +393,7 @@ __global__ __launch_bounds__(kThreads) void full_rows_kernel(FullArgs a, int fin
 template <typename E, int D>
 zp_status launch_full(FullArgs a, void* stream) {
   a.panels = ((a.n_cap + kB - 1) / kB + Geo<E, D>::kPanelTiles - 1) / Geo<E, D>::kPanelTiles;
-  const int64_t work = static_cast<int64_t>(a.units) * a.panels;
+  const int64_t work = static_cast<int64_t>(a.units) * ((a.panels + 1) / 2);
   const int64_t grid = (work + kXcds - 1) / kXcds * kXcds;
   if (grid > (1ll << 31) - 1)
     return zp::fail(ZP_EINVAL, "all-pairs redundancy: %lld workgroups",
