@@ -14,7 +14,9 @@
 //
 // The cosine matrix is symmetric, so every pair of tiles is formed once: a
 // panel takes the column tiles from its own first tile on and skips the
-// products below the diagonal. An off-diagonal product (row tile i, column
+// products below the diagonal. A workgroup runs panel p and then panel
+// P - 1 - p (a long and a short row of that triangle), so workgroups carry
+// about the same work. An off-diagonal product (row tile i, column
 // tile j > i) adds its row sums to tile i's tokens and its column sums to
 // tile j's, which belong to another wave or panel: all-token sums therefore
 // go to red_all by float atomic adds (zeroed before, divided by n - 1 after,
@@ -32,9 +34,9 @@
 // other tokens of its block (equal to the lightning score) and over all
 // other tokens.
 //
-// The panels of one unit read the same column tiles, so the workgroup ids
-// are dealt to XCDs (round robin on the device) such that consecutive panels
-// of a unit share one XCD and its L2.
+// The workgroups of one unit read the same column tiles, so the workgroup
+// ids are dealt to XCDs (round robin on the device) such that consecutive
+// workgroups of a unit share one XCD and its L2.
 #include <hip/hip_runtime.h>
 
 #include "zp_device.h"
