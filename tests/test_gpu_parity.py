@@ -882,3 +882,14 @@ def test_random_wide_shapes(seed):
     s = case.spec
     _check(case, f"wide random {seed}: n_max {s.n_max}, w {s.window}, "
                  f"G {s.q_heads // s.kv_heads}, S {s.shared_blocks}, flags {case.flags}")
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_wide_shapes_on_eight_waves(seed, monkeypatch):
+    # these sizes take the 4-wave workgroups by default; the same cases on
+    # the 8-wave shape
+    monkeypatch.setenv("ZIPAGE_KEY_GROUPS", "4")
+    case = _random_wide_case(seed)
+    s = case.spec
+    _check(case, f"wide random {seed} on 8 waves: n_max {s.n_max}, w {s.window}, "
+                 f"G {s.q_heads // s.kv_heads}, S {s.shared_blocks}, flags {case.flags}")
