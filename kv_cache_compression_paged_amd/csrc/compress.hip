@@ -441,6 +441,8 @@ void compress_kernel(ScoreArgs a) {
     if ((s & 1) == rg) {
       // squared norms sit on the Gram diagonal: column nl's is element
       // nl & 3 of lane (nl >> 2, nl); cos = g * rsqrt(max(|a|^2 |b|^2, 1e-16))
+      // (row rw = 4 jg + i's norm is in lane (jg, rw) of the same lane
+      // group, so all five reads take the diagonal directly, in parallel)
       const f32x4_t& gram = acc.g;
       const int di = nl & 3;
       const float own = di == 0 ? gram[0] : di == 1 ? gram[1] : di == 2 ? gram[2] : gram[3];
@@ -450,13 +452,15 @@ void compress_kernel(ScoreArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int rw = jg * 4 + i;
-        const float dr = __shfl(dg, rw, 64);                     // |k_rw|^2
+        const float dr = __shfl(own, jg * 20 + i, 64);           // |k_rw|^2
         if (rw != nl && rw < cnt && nl < cnt)
           cs += gram[i] * __builtin_amdgcn_rsqf(fmaxf(dr * dg, 1e-16f));
       }
       cs = zpd::pairsum16(cs);
       cs = zpd::pairsum32(cs);
-      if (jg == 0 && nl < cnt) s_tok[t] = cnt >= 2 ? cs / (cnt - 1) : 0.f;
+      // mean over the block's other keys (1/15 for a full block)
+      const float inv = cnt == kB ? 1.f / (kB - 1) : (cnt >= 2 ? 1.f / (cnt - 1) : 0.f);
+      if (jg == 0 && nl < cnt) s_tok[t] = cs * inv;
     }
   }, no_after, no_pair);
   // the 16 lanes sharing rows share the reference: their sums just add up
