@@ -409,10 +409,7 @@ void compress_kernel(ScoreArgs a) {
       for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float v = entry_ok(rt, i, t) ? acc.a[rt][i] * sl2 : -INFINITY;
-#pragma unroll
-          for (int o = 1; o < 16; o <<= 1) v = fmaxf(v, zpd::shfl_xor(v, o));
-          mr[rt][i] = v;
+          mr[rt][i] = zpd::max16(entry_ok(rt, i, t) ? acc.a[rt][i] * sl2 : -INFINITY);
         }
     }
     // One accumulation path for every block: in a masked block the entries
@@ -468,8 +465,7 @@ void compress_kernel(ScoreArgs a) {
   for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) z[rt][i] += zpd::shfl_xor(z[rt][i], o);
+      z[rt][i] = zpd::sum16(z[rt][i]);
       if (nl == 0 && rt < nrt) {
         st_m[kq][(rt0 + rt) * 16 + jg * 4 + i] = mr[rt][i];
         st_z[kq][(rt0 + rt) * 16 + jg * 4 + i] = z[rt][i];

@@ -147,15 +147,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     float p[4], alpha[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float tm = valid ? sc[i] : -INFINITY;
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) tm = fmaxf(tm, zpd::shfl_xor(tm, o));
+      const float tm = zpd::max16(valid ? sc[i] : -INFINITY);
       const float mn = fmaxf(m[i], tm);
       alpha[i] = (m[i] == -INFINITY) ? 0.f : zpd::fast_exp2((m[i] - mn) * a.sl2);
       p[i] = valid ? zpd::fast_exp2((sc[i] - mn) * a.sl2) : 0.f;
-      float rs = p[i];
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) rs += zpd::shfl_xor(rs, o);
+      const float rs = zpd::sum16(p[i]);
       z[i] = z[i] * alpha[i] + rs;
       m[i] = mn;
     }

@@ -115,6 +115,31 @@ __device__ __forceinline__ float shfl_xor(float v, int m) {
   return __shfl_xor(v, m, 64);
 }
 
+// Sum and maximum over each row of 16 lanes, in every lane of the row, on
+// the VALU (DPP): lane ^ 1 and lane ^ 2 by quad permutes, then the half-row
+// and row mirrors (lane 7 - i within 8, lane 15 - i within 16). Those pair
+// the same partial results as lane ^ 4 and lane ^ 8, and every pair is
+// added (or maxed) in one order, so the results equal the xor butterfly's
+// bit for bit, in all 16 lanes.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float sum16(float v) {
+  v += dpp_f32<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v += dpp_f32<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v += dpp_f32<0x141>(v);  // row_half_mirror
+  v += dpp_f32<0x140>(v);  // row_mirror
+  return v;
+}
+__device__ __forceinline__ float max16(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));
+  v = fmaxf(v, dpp_f32<0x4E>(v));
+  v = fmaxf(v, dpp_f32<0x141>(v));
+  v = fmaxf(v, dpp_f32<0x140>(v));
+  return v;
+}
+
 // v + v(lane ^ 16) and v + v(lane ^ 32) in every lane, on the VALU
 // (v_permlane16_swap / v_permlane32_swap exchange 16-lane rows / 32-lane
 // halves; with both operands equal, the two results hold the pair).
