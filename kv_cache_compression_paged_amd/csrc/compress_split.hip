@@ -472,8 +472,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
         float m = -INFINITY;
 #pragma unroll
         for (int b = 0; b < SB; ++b) m = fmaxf(m, acc[i][b][j]);
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, zpd::shfl_xor(m, o));
+        m = zpd::max16(m);
         const float msc = m * sl2;                 // the maximum, scaled (exp2 domain)
         const float nms = m == -INFINITY ? 0.f : -msc;
         float z = 0.f;
@@ -483,8 +482,7 @@ __global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
           acc[i][b][j] = e;
           z += e;
         }
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) z += zpd::shfl_xor(z, o);
+        z = zpd::sum16(z);
         mloc[i][j] = m == -INFINITY ? -INFINITY : msc;
         lsum[i][j] = m == -INFINITY ? -INFINITY : msc + __log2f(z);
       }

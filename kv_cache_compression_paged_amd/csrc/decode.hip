@@ -156,9 +156,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       m[i] = mn;
     }
     // P V: lane (vchunk, vq) accumulates keys s*RPI+vq for every head g
+    // (head g's statistics sit in lane (g >> 2) * 16, element g & 3)
 #pragma unroll
     for (int g = 0; g < GP; ++g) {
-      const float al = __shfl(alpha[g & 3], (g >> 2) * 16, 64);
+      const float al = __int_as_float(
+          __builtin_amdgcn_readlane(__float_as_int(alpha[g & 3]), (g >> 2) * 16));
 #pragma unroll
       for (int e = 0; e < VE; ++e) acc[g][e] *= al;
     }
@@ -196,7 +198,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     float* orow = a.out + (static_cast<int64_t>(r) * a.L + l) * a.Hq * D;
 #pragma unroll
     for (int g = 0; g < GP; ++g) {
-      const float zg = __shfl(z[g & 3], (g >> 2) * 16, 64);
+      const float zg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z[g & 3]), (g >> 2) * 16));
       if (vq == 0 && g < a.G) {
         float* dst = orow + static_cast<int64_t>(h * a.G + g) * D + vchunk * VE;
         const float inv = 1.f / zg;
@@ -211,8 +213,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     const int64_t pbase = static_cast<int64_t>(wid) * a.G;
 #pragma unroll
     for (int g = 0; g < GP; ++g) {
-      const float zg = __shfl(z[g & 3], (g >> 2) * 16, 64);
-      const float mg = __shfl(m[g & 3], (g >> 2) * 16, 64);
+      const float zg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z[g & 3]), (g >> 2) * 16));
+      const float mg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m[g & 3]), (g >> 2) * 16));
       if (vq == 0 && g < a.G) {
         float* dst = a.part_acc + (pbase + g) * D + vchunk * VE;
 #pragma unroll
