@@ -137,7 +137,7 @@ struct TileGeom {
   static constexpr int kLoads = kTileBytes / 1024;          // per block
   static constexpr int kLoadsPerWave = kLoads / 2;          // per wave of a pair
   static constexpr int kSwz = kRowChunks < 16 ? kRowChunks - 1 : 15;
-  static constexpr int kRing = NS;  // slots per quarter
+  static constexpr int kRing = NS;  // slots per key group
   static_assert(kLoadsPerWave >= 1, "tile too small");
   static_assert(kRing >= 4 && kRing <= 8, "ring length");
   static_assert((kRing - 1) * kLoadsPerWave <= 28, "wait count range");
@@ -150,7 +150,7 @@ struct TileGeom {
 template <typename E, int D, int RT, int NS, int KG>
 __global__ __launch_bounds__(threads_of(KG)) __attribute__((amdgpu_waves_per_eu(2)))
 void compress_kernel(ScoreArgs a) {
-  constexpr int kQuarters = KG;            // key groups: block kt goes to group kt mod KG
+  constexpr int kGroups = KG;              // key groups: block kt goes to group kt mod KG
   constexpr int kWaves = 2 * KG;           // two row halves per group
   constexpr int kThreads = threads_of(KG);
   using FragT = Frag<E, D>;
@@ -158,16 +158,16 @@ void compress_kernel(ScoreArgs a) {
   constexpr int kRows = RT * 16;
   constexpr int RTW = (RT + 1) / 2;     // row tiles of the first row half
   constexpr int kRing = TG::kRing;
-  __shared__ __attribute__((aligned(16))) char ring[kQuarters][kRing][TG::kTileBytes];
+  __shared__ __attribute__((aligned(16))) char ring[kGroups][kRing][TG::kTileBytes];
   extern __shared__ float s_tok[];  // [n_cap]: red, then order keys
   __shared__ int tab[1024];
   __shared__ float mprime[kRows];
   __shared__ int rowpos[kRows];
-  __shared__ float xchg[kQuarters][4][16];
+  __shared__ float xchg[kGroups][4][16];
   __shared__ int scratch[16];
   __shared__ int sel[2];
-  __shared__ float st_m[kQuarters][kRows];  // per-quarter row statistics
-  __shared__ float st_z[kQuarters][kRows];
+  __shared__ float st_m[kGroups][kRows];  // per-group row statistics
+  __shared__ float st_z[kGroups][kRows];
   // The ring is idle during the select (the column sweep ended with all
   // loads landed and a barrier): the per-wave histograms live in it then.
   // (Between the sweeps it is not idle: the column sweep starts on the
@@ -178,7 +178,7 @@ void compress_kernel(ScoreArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int kq = wave % kQuarters, rg = wave / kQuarters;
+  const int kq = wave % kGroups, rg = wave / kGroups;
   const int jg = lane >> 4, nl = lane & 15;
   const int u = blockIdx.x;
   const int h = u % a.Hkv;
@@ -249,13 +249,13 @@ void compress_kernel(ScoreArgs a) {
     rowpos[row] = row < a.wG ? n - a.w + row / a.G : -1;
 
   const float sl2 = a.sl2;
-  const int nsteps = (nt + kQuarters - 1) / kQuarters;
-  // Sweeps run forward or backward over a quarter's blocks; the backward
+  const int nsteps = (nt + kGroups - 1) / kGroups;
+  // Sweeps run forward or backward over a key group's blocks; the backward
   // column sweep starts with the blocks the row-statistics sweep read last
   // (the newest of them are still in the ring).
   bool backward = false;
-  int last_q = 0;  // last step with a block for this quarter (set below)
-  auto tile_of = [&](int s) { return (backward ? last_q - s : s) * kQuarters + kq; };
+  int last_q = 0;  // last step with a block for this key group (set below)
+  auto tile_of = [&](int s) { return (backward ? last_q - s : s) * kGroups + kq; };
   auto tile_masked = [&](int kt) {
     return (kt + 1) * kB > n || (causal && kt * kB + kB - 1 > n - a.w);
   };
@@ -277,8 +277,8 @@ void compress_kernel(ScoreArgs a) {
 #pragma unroll
   for (int c = 0; c < FragT::kChunks; ++c)
     frag_off[c] = TG::chunk_off(nl, jg * FragT::kChunks + c);
-  // last step that has a block for this quarter (-1: none)
-  const int last = kq < nt ? (nt - 1 - kq) / kQuarters : -1;
+  // last step that has a block for this key group (-1: none)
+  const int last = kq < nt ? (nt - 1 - kq) / kGroups : -1;
   last_q = last;
   struct Acc {
     f32x4_t a[RTW];
@@ -298,7 +298,7 @@ void compress_kernel(ScoreArgs a) {
     for (int c = 0; c < FragT::kChunks; ++c)
       f.v[c] = *reinterpret_cast<const zpd::u32x4_t*>(base + frag_off[c]);
   };
-  // One sweep over this quarter's blocks, two blocks (steps 2i and 2i+1)
+  // One sweep over this key group's blocks, two blocks (steps 2i and 2i+1)
   // per barrier. Loads run ahead through a ring of kRing slots: the prologue
   // issues steps 0..kRing-3 and iteration i refills the slots of steps 2i-2
   // and 2i-1 with steps 2i+kRing-2 and 2i+kRing-1. At iteration i the wave
@@ -475,7 +475,7 @@ void compress_kernel(ScoreArgs a) {
   bool redo = false;
   for (int row = tid; row < kRows; row += kThreads) {
     float mm = st_m[0][row], zz = st_z[0][row];
-    for (int v = 1; v < kQuarters; ++v) zpd::merge_stats(mm, zz, st_m[v][row], st_z[v][row], 1.f);
+    for (int v = 1; v < kGroups; ++v) zpd::merge_stats(mm, zz, st_m[v][row], st_z[v][row], 1.f);
     if (row < a.wG && !(zz > 0.f && zz < INFINITY && mm > -INFINITY)) redo = true;
     // p = exp2(x*sl2 - mprime) is the normalised probability of a row entry
     mprime[row] = (row < a.wG) ? mm + __log2f(zz) : INFINITY;
@@ -527,7 +527,7 @@ void compress_kernel(ScoreArgs a) {
     __syncthreads();
     for (int row = tid; row < kRows; row += kThreads) {
       float mm = st_m[0][row], zz = st_z[0][row];
-      for (int v = 1; v < kQuarters; ++v) zpd::merge_stats(mm, zz, st_m[v][row], st_z[v][row], 1.f);
+      for (int v = 1; v < kGroups; ++v) zpd::merge_stats(mm, zz, st_m[v][row], st_z[v][row], 1.f);
       mprime[row] = (row < a.wG && zz > 0.f) ? mm + __log2f(zz) : INFINITY;
     }
   }
