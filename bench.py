@@ -15,6 +15,10 @@ GB/s of the whole step, a roofline entry for the dominant kernel (kernel
 durations from HIP events recorded on the launch stream during the timed
 steps) and the CPU oracle timed on a bounded sample of the same workload.
 
+After that line's timed steps, the same run times the tiny, small-model,
+shared-prefix, long-context (8 requests of 16384 tokens) and overlap workloads
+and reports them under "other_workloads".
+
 With --workload overlap_512req_8grp the step is the two-stream case: 512
 requests in 8 groups, one group (64 requests, the query-slot holders) is
 compressed on stream C while the other 448 requests decode one token over all
@@ -956,7 +960,7 @@ def main():
         # (the largest pools need most of the device)
         ks, kw = min(args.steps, 20), min(args.warmup, 5)
         others = {}
-        for other in (synth.TINY, synth.SMALL, synth.PREFIX):
+        for other in (synth.TINY, synth.SMALL, synth.PREFIX, synth.LONG):
             others[other.name] = _brief(measure_compress(other, args, ks, kw, False,
                                                          with_copy=False, warm_min_s=0.3))
         ov = run_overlap(args, synth.OVERLAP, min(args.steps, 8), min(args.warmup, 2))

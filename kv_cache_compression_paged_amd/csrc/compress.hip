@@ -43,7 +43,7 @@
 // wave's own loads plus a raw s_barrier (a __syncthreads would drain every
 // load in flight). Two waves share a SIMD, so one's MFMA overlaps the
 // other's exp/VALU work. Long contexts (token rows that do not fit beside
-// the default 8-wave ring in LDS) take a 4-slot ring. The column sweep runs
+// the default 8-wave ring in LDS) take a 5-slot ring. The column sweep runs
 // backward: it starts on the blocks the first sweep read last and takes the
 // ones still in the ring without reloading them. In the column sweep the
 // two waves of a SIMD meet the barrier together, so for two unmasked blocks
@@ -99,7 +99,9 @@ constexpr int default_slots() {
   constexpr int n = 28 * 1024 / (16 * D * E::kBytes);
   return n > 8 ? 8 : (n < 4 ? 4 : n);
 }
-constexpr int kLongSlots = 4;
+// Long contexts: 5 slots (80 KiB for 4 KiB blocks) leave room for 16384
+// token rows beside the ring at every supported window size.
+constexpr int kLongSlots = 5;
 constexpr size_t kLdsPerCu = 160 * 1024;
 
 // s_waitcnt with vmcnt = n (0..28 or 32), expcnt untouched, lgkmcnt = 0.
@@ -967,7 +969,7 @@ int forced_key_groups() {
 
 // Two units per CU (KG = 2) when a unit's keys are at most 512 KiB and the
 // workgroup fits in half of a CU's LDS; otherwise one 8-wave workgroup per
-// CU (KG = 4) with the default ring, or the 4-slot ring when the token rows
+// CU (KG = 4) with the default ring, or the 5-slot ring when the token rows
 // do not fit beside it. The column sweep re-reads a unit's keys, mostly
 // from the last-level cache while every CU's units fit in it (256 MB): two
 // units of 512 KiB per CU are 256 MB across 256 CUs, larger units would

@@ -69,8 +69,9 @@ class Spec:
         return torch.float32 if self.dtype == "f32" else torch.bfloat16
 
 
-# The five workloads (sizes follow the 2048- and 4096-token KV budgets and an
-# 8B-class GQA layout).
+# The workloads (sizes follow the 2048- and 4096-token KV budgets and an
+# 8B-class GQA layout; the last one is a 16384-token budget, whose token rows
+# no longer fit in LDS beside the default key ring).
 TINY = Spec("tiny_fp32_1req", 1000, 1, 1, 2, 4, 64, 16, 8, 8, "f32", 8,
             permute=False)
 SMALL = Spec("small_28L_2kv_12q_N2048", 1001, 64, 28, 2, 12, 128, 16, 128, 32,
@@ -81,9 +82,11 @@ PREFIX = Spec("prefix_256req_4grp_32shared", 1003, 256, 32, 8, 32, 128, 16, 256,
               32, "bf16", 114560, near_dup=True, groups=4, shared_blocks=32)
 OVERLAP = Spec("overlap_512req_8grp", 1004, 512, 32, 8, 32, 128, 16, 256, 32,
                "bf16", 131072, near_dup=True, groups=8, compress_groups=8)
+LONG = Spec("long_8req_32L_8kv_N16384", 1005, 8, 32, 8, 32, 128, 16, 1024, 32,
+            "bf16", 8192, near_dup=True)
 
 SPECS: Dict[str, Spec] = {s.name: s for s in (TINY, SMALL, EIGHT_B, PREFIX,
-                                              OVERLAP)}
+                                              OVERLAP, LONG)}
 
 
 def scaled(spec: Spec, **kw) -> Spec:

@@ -80,10 +80,10 @@ def test_fp32_head_dim_128():
 
 def test_long_context_takes_the_short_ring():
     # 16384 tokens: the token rows (64 KiB) no longer fit beside the default
-    # 7-slot key ring in LDS, so the launcher picks the 4-slot ring
+    # 7-slot key ring in LDS, so the launcher picks the 5-slot ring
     spec = synth.scaled(synth.EIGHT_B, requests=1, layers=1, kv_heads=2,
                         q_heads=8, n_max=1024, pool_blocks=1024 + 8)
-    _check(P.Case(spec), "n = 16384 (4-slot ring)")
+    _check(P.Case(spec), "n = 16384 (5-slot ring)")
 
 
 def test_fp32_d128_n_cap_beyond_lds_is_rejected():
