@@ -534,6 +534,12 @@ def test_full_size_8b_split():
     _full_size(synth.EIGHT_B, 64, 14, fused=True, flags=Z.ZP_SPLIT_UNITS)
 
 
+def test_full_size_long_context():
+    # 8 requests of 16384 tokens (2048 units): the 5-slot ring, launched as
+    # the bench times it (fused update)
+    _full_size(synth.LONG, 16, 15, fused=True)
+
+
 def test_full_size_prefix():
     # 256 requests in 4 groups sharing 32 leading blocks each: the pinned
     # prefix stays in place and the kept private rows go to fresh targets
