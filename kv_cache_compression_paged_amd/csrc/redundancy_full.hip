@@ -183,8 +183,7 @@ void redundancy_full_kernel(FullArgs a) {
       else
         A[rt].zero();
       float own = A[rt].sumsq();
-      own += zpd::shfl_xor(own, 16);
-      own += zpd::shfl_xor(own, 32);
+      own = zpd::pairsum32(zpd::pairsum16(own));
       if (grt < nt && row < n) rmin2 = fminf(rmin2, own);
       if (jg == 0) rnorm2[wave][rt][nl] = own;
 #pragma unroll
@@ -259,16 +258,64 @@ void redundancy_full_kernel(FullArgs a) {
           read_frag(f, slot, wave);
           const bool ok = ct * kB + nl < n;
           float sq = ok ? f.sumsq() : 0.f;
-          sq += zpd::shfl_xor(sq, 16);
-          sq += zpd::shfl_xor(sq, 32);
-          float mn = ok ? sq : INFINITY;
-#pragma unroll
-          for (int o = 1; o < 16; o <<= 1) mn = fminf(mn, zpd::shfl_xor(mn, o));
+          sq = zpd::pairsum32(zpd::pairsum16(sq));
+          const float mn = -zpd::max16(-(ok ? sq : INFINITY));  // row minimum
           if (jg == 0) cn2[s & 1][wave][nl] = sq;
           if (lane == 0) cmin[s & 1][wave] = mn;
         }
       }
       lds_barrier();
+      // A step whose four column tiles all lie past this wave's row tiles,
+      // inside n, and clear the norm clamp needs none of the guards below:
+      // it takes one branch-free body in which the next tile's products are
+      // issued before this tile's sums, so the MFMA chains overlap the vector
+      // work. It adds exactly what the general path adds, in the same order.
+      const int ct0 = tile0 + 4 * s;
+      bool fast = false;
+      if constexpr (E::kBytes == 2) {
+        const float cmin4 = fminf(fminf(cmin[s & 1][0], cmin[s & 1][1]),
+                                  fminf(cmin[s & 1][2], cmin[s & 1][3]));
+        fast = all_pairs && ct0 + 4 <= ct_end && ct0 > tile0 + wave * RT + RT - 1 &&
+               (ct0 + 4) * kB <= n && rmin2 * cmin4 >= 1e-16f;
+      }
+      if (fast) {
+        if constexpr (E::kBytes == 2) {
+          float cinv4[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) cinv4[c] = __builtin_amdgcn_rsqf(cn2[s & 1][c][nl]);
+          f32x4_t g[2][RT];
+          auto products = [&](int c) {
+            FragT f;
+            read_frag(f, slot, c);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) g[c & 1][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k = 0; k < FragT::kChunks; ++k)
+#pragma unroll
+              for (int rt = 0; rt < RT; ++rt)
+                g[c & 1][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(zpd::bf16x8_t, A[rt].v[k]),
+                    __builtin_bit_cast(zpd::bf16x8_t, f.v[k]), g[c & 1][rt], 0, 0, 0);
+          };
+          products(0);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            if (c + 1 < 4) products(c + 1);
+            float colf = 0.f;
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                fact[rt][i] = fmaf(g[c & 1][rt][i], cinv4[c], fact[rt][i]);
+                colf = fmaf(g[c & 1][rt][i], rinv[rt][i], colf);
+              }
+            // the column's sum, the same in all four lane groups (each
+            // writes it: no branch in this body)
+            const float cs = zpd::pairsum32(zpd::pairsum16(colf * cinv4[c]));
+            colw[s & 1][wave][c][nl] = cs;
+          }
+        }
+      } else {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int ct = tile0 + 4 * s + c;
@@ -343,11 +390,10 @@ void redundancy_full_kernel(FullArgs a) {
         }
         if (all_pairs) {
           // the 16 rows of a column sit in the four lane groups
-          float cs = fmaf(colf, cinv, colx);
-          cs += zpd::shfl_xor(cs, 16);
-          cs += zpd::shfl_xor(cs, 32);
+          const float cs = zpd::pairsum32(zpd::pairsum16(fmaf(colf, cinv, colx)));
           if (jg == 0) colw[s & 1][wave][c][nl] = cs;
         }
+      }
       }
     }
     lds_barrier();  // the last step's column sums are complete
@@ -360,12 +406,9 @@ void redundancy_full_kernel(FullArgs a) {
       const int grt = tile0 + wave * RT + rt;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-          fact[rt][i] += zpd::shfl_xor(fact[rt][i], o);
-          exact[rt][i] += zpd::shfl_xor(exact[rt][i], o);
-          blk[rt][i] += zpd::shfl_xor(blk[rt][i], o);
-        }
+        fact[rt][i] = zpd::sum16(fact[rt][i]);
+        exact[rt][i] = zpd::sum16(exact[rt][i]);
+        blk[rt][i] = zpd::sum16(blk[rt][i]);
         const int row = grt * kB + 4 * jg + i;
         if (nl == 0 && grt < nt && row < n) {
           const int cnt = min(kB, n - grt * kB);
