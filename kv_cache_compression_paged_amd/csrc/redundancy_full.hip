@@ -317,83 +317,83 @@ void redundancy_full_kernel(FullArgs a) {
         }
       } else {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int ct = tile0 + 4 * s + c;
-        if (ct >= ct_end) break;
-        const int col = ct * kB + nl;
-        const bool ok = col < n;
-        FragT f;
-        read_frag(f, slot, c);
-        if (!ok) f.zero();
-        const float c2 = cn2[s & 1][c][nl];
-        const bool safe = rmin2 * cmin[s & 1][c] >= 1e-16f;
-        const float cinv = (ok && safe) ? __builtin_amdgcn_rsqf(c2) : 0.f;
-        // which of this wave's row tiles pair with column tile ct: those at or
-        // below it (at it only, without red_all); the others were or will be
-        // formed as (ct, row tile) by the owner of ct
-        bool use[RT];
+        for (int c = 0; c < 4; ++c) {
+          const int ct = tile0 + 4 * s + c;
+          if (ct >= ct_end) break;
+          const int col = ct * kB + nl;
+          const bool ok = col < n;
+          FragT f;
+          read_frag(f, slot, c);
+          if (!ok) f.zero();
+          const float c2 = cn2[s & 1][c][nl];
+          const bool safe = rmin2 * cmin[s & 1][c] >= 1e-16f;
+          const float cinv = (ok && safe) ? __builtin_amdgcn_rsqf(c2) : 0.f;
+          // which of this wave's row tiles pair with column tile ct: those at or
+          // below it (at it only, without red_all); the others were or will be
+          // formed as (ct, row tile) by the owner of ct
+          bool use[RT];
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          const int grt = tile0 + wave * RT + rt;
-          use[rt] = grt < nt && (all_pairs ? grt <= ct : grt == ct);
-        }
-        f32x4_t g[RT];
+          for (int rt = 0; rt < RT; ++rt) {
+            const int grt = tile0 + wave * RT + rt;
+            use[rt] = grt < nt && (all_pairs ? grt <= ct : grt == ct);
+          }
+          f32x4_t g[RT];
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) g[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        // past the wave's last row tile every row tile pairs with ct (rows
-        // beyond n are zero fragments): the products run unguarded
-        const bool every = all_pairs && ct >= tile0 + wave * RT + RT - 1;
-        if constexpr (E::kBytes == 2) {
-          // chunk-major: the RT accumulation chains interleave
-          if (every) {
+          for (int rt = 0; rt < RT; ++rt) g[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          // past the wave's last row tile every row tile pairs with ct (rows
+          // beyond n are zero fragments): the products run unguarded
+          const bool every = all_pairs && ct >= tile0 + wave * RT + RT - 1;
+          if constexpr (E::kBytes == 2) {
+            // chunk-major: the RT accumulation chains interleave
+            if (every) {
 #pragma unroll
-            for (int k = 0; k < FragT::kChunks; ++k)
+              for (int k = 0; k < FragT::kChunks; ++k)
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+                  g[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                      __builtin_bit_cast(zpd::bf16x8_t, A[rt].v[k]),
+                      __builtin_bit_cast(zpd::bf16x8_t, f.v[k]), g[rt], 0, 0, 0);
+            } else {
 #pragma unroll
               for (int rt = 0; rt < RT; ++rt)
-                g[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(zpd::bf16x8_t, A[rt].v[k]),
-                    __builtin_bit_cast(zpd::bf16x8_t, f.v[k]), g[rt], 0, 0, 0);
+                if (use[rt]) g[rt] = zpd::mma_rows<E, D>(A[rt], f, f32x4_t{0.f, 0.f, 0.f, 0.f});
+            }
           } else {
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
-              if (use[rt]) g[rt] = zpd::mma_rows<E, D>(A[rt], f, f32x4_t{0.f, 0.f, 0.f, 0.f});
+              if (every || use[rt]) g[rt] = zpd::mma_rows<E, D>(A[rt], f, f32x4_t{0.f, 0.f, 0.f, 0.f});
           }
-        } else {
+          float colf = 0.f, colx = 0.f;  // this lane's share of column nl's sums
 #pragma unroll
-          for (int rt = 0; rt < RT; ++rt)
-            if (every || use[rt]) g[rt] = zpd::mma_rows<E, D>(A[rt], f, f32x4_t{0.f, 0.f, 0.f, 0.f});
-        }
-        float colf = 0.f, colx = 0.f;  // this lane's share of column nl's sums
+          for (int rt = 0; rt < RT; ++rt) {
+            if (!use[rt]) continue;
+            const int grt = tile0 + wave * RT + rt;
+            if (ct != grt && safe) {
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          if (!use[rt]) continue;
-          const int grt = tile0 + wave * RT + rt;
-          if (ct != grt && safe) {
+              for (int i = 0; i < 4; ++i) {
+                fact[rt][i] = fmaf(g[rt][i], cinv, fact[rt][i]);
+                colf = fmaf(g[rt][i], rinv[rt][i], colf);
+              }
+            } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              fact[rt][i] = fmaf(g[rt][i], cinv, fact[rt][i]);
-              colf = fmaf(g[rt][i], rinv[rt][i], colf);
-            }
-          } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int row = grt * kB + 4 * jg + i;
-              const float r2 = rnorm2[wave][rt][4 * jg + i];
-              const float cv = (ok && row != col)
-                                   ? g[rt][i] * __builtin_amdgcn_rsqf(fmaxf(r2 * c2, 1e-16f))
-                                   : 0.f;
-              exact[rt][i] += cv;
-              if (ct == grt) blk[rt][i] += cv;
-              else colx += cv;
+              for (int i = 0; i < 4; ++i) {
+                const int row = grt * kB + 4 * jg + i;
+                const float r2 = rnorm2[wave][rt][4 * jg + i];
+                const float cv = (ok && row != col)
+                                     ? g[rt][i] * __builtin_amdgcn_rsqf(fmaxf(r2 * c2, 1e-16f))
+                                     : 0.f;
+                exact[rt][i] += cv;
+                if (ct == grt) blk[rt][i] += cv;
+                else colx += cv;
+              }
             }
           }
+          if (all_pairs) {
+            // the 16 rows of a column sit in the four lane groups
+            const float cs = zpd::pairsum32(zpd::pairsum16(fmaf(colf, cinv, colx)));
+            if (jg == 0) colw[s & 1][wave][c][nl] = cs;
+          }
         }
-        if (all_pairs) {
-          // the 16 rows of a column sit in the four lane groups
-          const float cs = zpd::pairsum32(zpd::pairsum16(fmaf(colf, cinv, colx)));
-          if (jg == 0) colw[s & 1][wave][c][nl] = cs;
-        }
-      }
       }
     }
     lds_barrier();  // the last step's column sums are complete
