@@ -78,12 +78,30 @@ def test_fp32_head_dim_128():
     _check(P.Case(F32_D128), "fp32 d=128")
 
 
+LONG = synth.scaled(synth.EIGHT_B, requests=1, layers=1, kv_heads=2,
+                    q_heads=8, n_max=1024, pool_blocks=1024 + 8)
+
+
 def test_long_context_takes_the_short_ring():
     # 16384 tokens: the token rows (64 KiB) no longer fit beside the default
     # 7-slot key ring in LDS, so the launcher picks the 5-slot ring
-    spec = synth.scaled(synth.EIGHT_B, requests=1, layers=1, kv_heads=2,
-                        q_heads=8, n_max=1024, pool_blocks=1024 + 8)
-    _check(P.Case(spec), "n = 16384 (5-slot ring)")
+    _check(P.Case(LONG), "n = 16384 (5-slot ring)")
+
+
+def test_long_context_fp32_d64():
+    # fp32 rows of head_dim 64 are 4 KiB blocks as well: 16384 tokens take
+    # the 5-slot ring in that element type too
+    spec = synth.scaled(synth.TINY, requests=1, layers=1, kv_heads=2, q_heads=4,
+                        n_max=1024, window=16, pool_blocks=1024 + 8, permute=True)
+    _check(P.Case(spec), "fp32 d=64, n = 16384 (5-slot ring)")
+
+
+def test_long_context_window_rows_192():
+    # the largest window (w*G = 192) beside 16384 token rows: the 5-slot
+    # ring's static LDS is largest here and must still fit
+    spec = synth.scaled(synth.SMALL, requests=1, layers=1, n_max=1024,
+                        pool_blocks=1024 + 8)
+    _check(P.Case(spec), "192 window rows, n = 16384 (5-slot ring)")
 
 
 def test_fp32_d128_n_cap_beyond_lds_is_rejected():
@@ -144,6 +162,7 @@ SHAPE_CASES = [
                                  max_blocks=EIGHT_B.n_max + 3)),
     ("shared prefix", lambda: P.Case(PREFIX, use_block_manager=True)),
     ("fused update", lambda: P.Case(EIGHT_B, flags=Z.ZP_UPDATE_GLOBAL)),
+    ("16384 tokens", lambda: P.Case(LONG)),
 ]
 
 
